@@ -1,0 +1,14 @@
+"""CPU oracle for tree-verification attention -- TEST INFRASTRUCTURE.
+
+Only the test suite, the smoke check in ``__graft_entry__`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The product path
+(the HIP library and its Python binding) never imports it, and it imports
+nothing from the product path.
+"""
+from .oracle import (  # noqa: F401
+    build_oracle,
+    mask_bits,
+    mask_anchor,
+    tree_attn,
+    accept,
+)

@@ -1,0 +1,160 @@
+"""ctypes front end of the plain-C oracle (``tv_oracle.c``) -- TEST INFRASTRUCTURE.
+
+Only the test suite, ``__graft_entry__.smoke()`` and ``bench.py``'s
+CPU-baseline leg may import this module.  It shares no code with the HIP
+library: it compiles its own C source with gcc and hands it numpy arrays.
+
+All floating point in the C code is double precision; float inputs arrive as
+float32 arrays holding exactly the values the GPU gets (bf16 values upcast).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "tv_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+# A test may point the front end at a deliberately mutated build of the same
+# source (to show the pins catch planted mistakes); nothing else sets this.
+_LIB_OVERRIDE = os.environ.get("TV_ORACLE_LIB")
+_lib = None
+
+
+def build_oracle(force: bool = True) -> str:
+    """Compile ``tv_oracle.c`` into ``liboracle.so`` (plain gcc, IEEE math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-Wall", "-Werror",
+             "-fno-fast-math", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build_oracle(force=True)
+            lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int32
+        lib.orc_mask_bits.argtypes = [P, P, I, I, P, P, P]
+        lib.orc_mask_bits.restype = None
+        lib.orc_mask_anchor.argtypes = [P, P, I, P, P, P, P]
+        lib.orc_mask_anchor.restype = None
+        lib.orc_tree_attn.argtypes = [I, P, P, P, P, I, P, P, P, I, I, I, I, I,
+                                      ctypes.c_double, P, I, P, P]
+        lib.orc_tree_attn.restype = ctypes.c_int
+        lib.orc_accept.argtypes = [P, P, P, P, I, I, P, P, P]
+        lib.orc_accept.restype = None
+        _lib = lib
+    return _lib
+
+
+def _np(x, dtype):
+    """torch tensor or array-like -> C-contiguous numpy array of ``dtype``."""
+    if hasattr(x, "detach"):
+        x = x.detach().cpu()
+        if str(x.dtype) == "torch.bfloat16":
+            x = x.float()
+        x = x.numpy()
+    return np.ascontiguousarray(np.asarray(x), dtype=dtype)
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def mask_bits(parent, cu_nodes, words: int):
+    """Ancestor bitmask per node: returns (bits uint64 [N, words], depth int32 [N], err int32 [B])."""
+    lib = _load()
+    parent = _np(parent, np.int32)
+    cu = _np(cu_nodes, np.int32)
+    batch = len(cu) - 1
+    n = int(cu[-1])
+    bits = np.zeros((n, words), np.uint64)
+    depth = np.zeros(n, np.int32)
+    err = np.zeros(batch, np.int32)
+    lib.orc_mask_bits(_p(parent), _p(cu), batch, words, _p(bits), _p(depth), _p(err))
+    return bits, depth, err
+
+
+def mask_anchor(parent, cu_nodes):
+    """Anchor form: returns (anchor_pos, branch_depth, depth, err), int32."""
+    lib = _load()
+    parent = _np(parent, np.int32)
+    cu = _np(cu_nodes, np.int32)
+    batch = len(cu) - 1
+    n = int(cu[-1])
+    ap = np.zeros(n, np.int32)
+    bd = np.zeros(n, np.int32)
+    depth = np.zeros(n, np.int32)
+    err = np.zeros(batch, np.int32)
+    lib.orc_mask_anchor(_p(parent), _p(cu), batch, _p(ap), _p(bd), _p(depth), _p(err))
+    return ap, bd, depth, err
+
+
+def tree_attn(q, k_cache, v_cache, block_table, prefix_len, cu_nodes, parent,
+              num_q_heads: int, num_kv_heads: int, scale: float, rows=None,
+              formulation: str = "dense"):
+    """Attention of every (node, head) row -- or of the listed ``rows`` -- in fp64.
+
+    ``q`` is [N, Hq, D]; caches are [pages, Hkv, page_size, D]; ``rows`` is an
+    optional int array [R, 2] of (global node, q head).  Returns
+    (out float64 [N, Hq, D] or [R, D], lse float64 [N, Hq] or [R]).
+    """
+    lib = _load()
+    q = _np(q, np.float32)
+    kc = _np(k_cache, np.float32)
+    vc = _np(v_cache, np.float32)
+    bt = _np(block_table, np.int32)
+    pl = _np(prefix_len, np.int32)
+    cu = _np(cu_nodes, np.int32)
+    par = _np(parent, np.int32)
+    batch = len(cu) - 1
+    n = int(cu[-1])
+    d = q.shape[-1]
+    page = kc.shape[2]
+    assert q.shape == (n, num_q_heads, d)
+    assert kc.shape[1] == num_kv_heads and kc.shape[3] == d and vc.shape == kc.shape
+    assert bt.ndim == 2 and bt.shape[0] == batch
+    if rows is None:
+        out = np.zeros((n, num_q_heads, d), np.float64)
+        lse = np.zeros((n, num_q_heads), np.float64)
+        rp, nr = None, 0
+    else:
+        rows = _np(rows, np.int32).reshape(-1, 2)
+        out = np.zeros((rows.shape[0], d), np.float64)
+        lse = np.zeros(rows.shape[0], np.float64)
+        rp, nr = _p(rows), rows.shape[0]
+    form = {"dense": 0, "path": 1}[formulation]
+    rc = lib.orc_tree_attn(form, _p(q), _p(kc), _p(vc), _p(bt), bt.shape[1], _p(pl),
+                           _p(cu), _p(par), batch, num_q_heads, num_kv_heads, d, page,
+                           float(scale), rp, nr, _p(out), _p(lse))
+    if rc != 0:
+        raise ValueError("oracle rejected the attention arguments")
+    return out, lse
+
+
+def accept(parent, draft_tok, target_tok, cu_nodes, max_depth: int):
+    """Greedy acceptance: returns (accept_len [B], path [B, max_depth+1], bonus [B])."""
+    lib = _load()
+    par = _np(parent, np.int32)
+    dr = _np(draft_tok, np.int32)
+    tg = _np(target_tok, np.int32)
+    cu = _np(cu_nodes, np.int32)
+    batch = len(cu) - 1
+    al = np.zeros(batch, np.int32)
+    path = np.zeros((batch, max_depth + 1), np.int32)
+    bonus = np.zeros(batch, np.int32)
+    lib.orc_accept(_p(par), _p(dr), _p(tg), _p(cu), batch, max_depth, _p(al), _p(path),
+                   _p(bonus))
+    return al, path, bonus

@@ -1,0 +1,45 @@
+"""The oracle pins are sensitive: each plausible mistake planted in a copy of
+the oracle's C source (a dropped term, a wrong index, a flipped comparison)
+makes the pin suite fail.  Everything here runs on the CPU."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "tv_oracle.c")
+
+MUTANTS = {
+    "gqa_map_modulo": ("int g = h / (a->hq / a->hkv);", "int g = h % a->hkv;"),
+    "scale_dropped": ("scores[p] = a->scale * orc_dot(", "scores[p] = orc_dot("),
+    "no_self_attention": ("for (int j = i; j != -1; j = par[j]) vis[j] = 1;",
+                          "for (int j = par[i]; j != -1; j = par[j]) vis[j] = 1;"),
+    "prefix_off_by_one": ("int visible = p < P || vis[p - P];",
+                          "int visible = p < P - 1 || (p >= P && vis[p - P]);"),
+    "lse_missing_max": ("  *lse = m + log(l);\n}\n\n/* Path-gather", "  *lse = log(l);\n}\n\n/* Path-gather"),
+    "page_slot_swapped": ("int slot = pos % a->page;", "int slot = pos / a->page;"),
+    "match_own_target": ("if (dr[j] != tg[par[j]]) ok = 0;", "if (dr[j] != tg[j]) ok = 0;"),
+    "tie_to_largest_index": ("if (ok && dep > best_depth)", "if (ok && dep >= best_depth)"),
+    "depth_off_by_one": ("      int d = -1;\n", "      int d = 0;\n"),
+    "anchor_depth_reset": ("branch_depth[n0 + i] = branch_depth[n0 + i - 1] + 1;",
+                           "branch_depth[n0 + i] = 1;"),
+    "second_root_accepted": ("if (par[i] < 0 || par[i] >= i) return 1;",
+                             "if (par[i] < -1 || par[i] >= i) return 1;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_oracle_mistake_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, "mutation anchor not found: " + name
+    mut = tmp_path / "mutant.c"
+    mut.write_text(src.replace(old, new))
+    lib = tmp_path / "mutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", str(mut), "-o", str(lib), "-lm"])
+    env = dict(os.environ, TV_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, "pins did not catch mutant %s:\n%s" % (name, r.stdout[-2000:])

@@ -1,0 +1,384 @@
+"""Pins of the CPU oracle to facts fixed outside it (no GPU needed).
+
+Each test checks the oracle against something the pages or the mathematics
+fix independently of its C code: a worked illustration from a page, a closed
+form, a special case that a library routine computes (torch's
+scaled_dot_product_attention in float64), an invariant the pages state, or a
+brute force written differently (boolean matrix closure, greedy descent).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def closure(parent):
+    """Reflexive-transitive closure of child->parent by boolean matrix powers."""
+    n = len(parent)
+    A = np.zeros((n, n), bool)
+    for i in range(1, n):
+        A[i, parent[i]] = True
+    R = np.eye(n, dtype=bool)
+    while True:
+        R2 = R | ((R.astype(np.int64) @ A.astype(np.int64)) > 0)
+        if (R2 == R).all():
+            return R
+        R = R2
+
+
+def bits_to_dense(bits, n):
+    out = np.zeros((n, n), bool)
+    for i in range(n):
+        for j in range(n):
+            out[i, j] = (int(bits[i, j // 64]) >> (j % 64)) & 1
+    return out
+
+
+# ------------------------------------------------------------------ masks --
+
+def test_mask_chain_is_lower_triangular(oracle_lib):
+    n = 100
+    par = [-1] + list(range(n - 1))
+    bits, depth, err = oracle.mask_bits(par, [0, n], 2)
+    assert err.tolist() == [0]
+    assert (bits_to_dense(bits, n) == np.tril(np.ones((n, n), bool))).all()
+    assert depth.tolist() == list(range(n))
+
+
+def test_mask_star_is_diagonal_plus_root(oracle_lib):
+    n = 40
+    par = [-1] + [0] * (n - 1)
+    bits, depth, err = oracle.mask_bits(par, [0, n], 1)
+    expect = np.eye(n, dtype=bool)
+    expect[:, 0] = True
+    assert (bits_to_dense(bits, n) == expect).all()
+    assert depth.tolist() == [0] + [1] * (n - 1)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_mask_matches_matrix_closure(oracle_lib, seed):
+    rng = np.random.default_rng(seed)
+    trees = [W.random_tree(rng, int(n)) for n in rng.integers(1, 200, size=4)]
+    cu = np.concatenate([[0], np.cumsum([len(t) for t in trees])]).astype(np.int32)
+    bits, depth, err = oracle.mask_bits(np.concatenate(trees), cu, 4)
+    assert (err == 0).all()
+    for b, t in enumerate(trees):
+        R = closure(t)
+        got = bits_to_dense(bits[cu[b]:cu[b + 1]], len(t))
+        assert (got == R).all()
+        assert (depth[cu[b]:cu[b + 1]] == R.sum(1) - 1).all()
+
+
+@pytest.mark.parametrize("bad", [
+    [0, 0, 1],          # root does not have parent -1
+    [-1, 0, 2],         # parent equal to self
+    [-1, 0, 3, 1],      # parent after the node (would allow a cycle)
+    [-1, 0, -1],        # a second root
+    [-1, -2, 0],        # out of range
+])
+def test_mask_rejects_malformed_trees(oracle_lib, bad):
+    good = [-1, 0, 0, 1]
+    par = np.array(good + bad, np.int32)
+    cu = [0, len(good), len(good) + len(bad)]
+    bits, depth, err = oracle.mask_bits(par, cu, 1)
+    assert err.tolist() == [0, 1]
+    assert (bits[len(good):] == 0).all() and (depth[len(good):] == -1).all()
+    ap, bd, dep, err2 = oracle.mask_anchor(par, cu)
+    assert err2.tolist() == [0, 1]
+
+
+def test_mask_rejects_tree_wider_than_words(oracle_lib):
+    n = 65
+    par = [-1] + list(range(n - 1))
+    _, _, err = oracle.mask_bits(par, [0, n], 1)
+    assert err.tolist() == [1]
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_anchor_form_equals_closure(oracle_lib, seed):
+    rng = np.random.default_rng(100 + seed)
+    trees = []
+    for _ in range(3):
+        trunk = int(rng.integers(1, 120))
+        nb = int(rng.integers(0, 8))
+        anchors = np.sort(rng.integers(0, trunk, size=nb))
+        if nb:
+            anchors[-1] = trunk - 1          # a branch at the last trunk node
+        par = W.trunk_branch_tree(trunk, anchors.tolist(), int(rng.integers(1, 20)))
+        trees.append(par)
+    cu = np.concatenate([[0], np.cumsum([len(t) for t in trees])]).astype(np.int32)
+    ap, bd, depth, err = oracle.mask_anchor(np.concatenate(trees), cu)
+    assert (err == 0).all()
+    for b, t in enumerate(trees):
+        n = len(t)
+        R = closure(t)
+        a, d = ap[cu[b]:cu[b + 1]], bd[cu[b]:cu[b + 1]]
+        i = np.arange(n)[:, None]
+        j = np.arange(n)[None, :]
+        vis = (j <= a[:, None]) | ((j > i - d[:, None]) & (j <= i))
+        assert (vis == R).all()
+        assert (depth[cu[b]:cu[b + 1]] == R.sum(1) - 1).all()
+
+
+def test_anchor_form_rejects_branch_of_branch(oracle_lib):
+    par = W.trunk_branch_tree(10, [3, 7], 4)
+    par.append(len(par) - 3)                # hangs off the middle of a branch
+    _, _, _, err = oracle.mask_anchor(par, [0, len(par)])
+    assert err.tolist() == [2]
+
+
+# -------------------------------------------------------------- attention --
+
+def gathered_kv(w, b):
+    """Contiguous [Hkv, P+n, D] float64 K and V of request b, read through its page table."""
+    L = int(w.prefix_len[b]) + int(w.nodes_per_request[b])
+    pos = np.arange(L)
+    pages = torch.from_numpy(w.block_table[b, pos // w.page_size].astype(np.int64))
+    slots = torch.from_numpy(pos % w.page_size)
+    k = w.k_cache.double()[pages, :, slots, :].permute(1, 0, 2)
+    v = w.v_cache.double()[pages, :, slots, :].permute(1, 0, 2)
+    return k, v
+
+
+def sdpa_reference(w, b, vis_tree):
+    """torch float64 SDPA for request b with boolean tree visibility [n, n];
+    prefix keys visible to every node; KV heads repeated per GQA group."""
+    P, n = int(w.prefix_len[b]), int(w.nodes_per_request[b])
+    k, v = gathered_kv(w, b)
+    G = w.num_q_heads // w.num_kv_heads
+    k = k.repeat_interleave(G, 0)
+    v = v.repeat_interleave(G, 0)
+    q = w.q.double()[w.cu_nodes[b]:w.cu_nodes[b + 1]].permute(1, 0, 2)   # [Hq, n, D]
+    mask = torch.cat([torch.ones(n, P, dtype=torch.bool), torch.from_numpy(vis_tree)], 1)
+    out = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=w.scale)
+    s = (q @ k.transpose(1, 2)) * w.scale
+    s = s.masked_fill(~mask, -math.inf)
+    lse = torch.logsumexp(s, -1)
+    return out.permute(1, 0, 2).numpy(), lse.permute(1, 0).numpy()
+
+
+def small(parent_lists, prefix, hq=8, hkv=2, d=32, seed=0, **kw):
+    return W.build_workload("pin", parent_lists, prefix, hq, hkv, d, "f32", seed, **kw)
+
+
+def test_chain_tree_equals_causal_attention(oracle_lib):
+    n, P = 23, 37
+    w = small([[-1] + list(range(n - 1))], [P], seed=1, permute_pages=True)
+    out, lse = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_len,
+                                w.cu_nodes, w.parent, 8, 2, w.scale)
+    ref, rlse = sdpa_reference(w, 0, np.tril(np.ones((n, n), bool)))
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_tree_attention_equals_sdpa_with_closure_mask(oracle_lib, seed):
+    rng = np.random.default_rng(seed)
+    trees = [W.random_tree(rng, int(n), max_children=4) for n in (1, 17, 60)]
+    prefix = [int(p) for p in rng.integers(0, 90, size=3)]
+    w = small(trees, prefix, hq=6, hkv=3, d=16, seed=seed, permute_pages=True, spare_pages=3)
+    for form in ("dense", "path"):
+        out, lse = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_len,
+                                    w.cu_nodes, w.parent, 6, 3, w.scale, formulation=form)
+        for b, t in enumerate(trees):
+            ref, rlse = sdpa_reference(w, b, closure(t))
+            sl = slice(w.cu_nodes[b], w.cu_nodes[b + 1])
+            np.testing.assert_allclose(out[sl], ref, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[sl], rlse, rtol=0, atol=1e-12)
+
+
+def test_single_node_no_prefix_returns_its_own_value(oracle_lib):
+    w = small([[-1]], [0], seed=3)
+    out, lse = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_len,
+                                w.cu_nodes, w.parent, 8, 2, w.scale)
+    for h in range(8):
+        g = h // 4
+        np.testing.assert_array_equal(out[0, h], w.v_cache[0, g, 0].double().numpy())
+        s = float((w.q[0, h].double() * w.k_cache[0, g, 0].double()).sum()) * w.scale
+        assert abs(lse[0, h] - s) < 1e-12
+
+
+def test_equal_keys_give_mean_of_visible_values(oracle_lib):
+    rng = np.random.default_rng(7)
+    tree = W.random_tree(rng, 30)
+    P = 50
+    w = small([tree], [P], seed=7)
+    w.k_cache[:] = w.k_cache[0, :, 0:1, :]     # every key of a kv head identical
+    out, lse = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_len,
+                                w.cu_nodes, w.parent, 8, 2, w.scale)
+    k, v = gathered_kv(w, 0)
+    R = closure(tree)
+    for i in range(len(tree)):
+        keys = list(range(P)) + [P + j for j in range(len(tree)) if R[i, j]]
+        for h in range(8):
+            g = h // 4
+            np.testing.assert_allclose(out[i, h], v[g, keys].mean(0).numpy(), atol=1e-12)
+            s = float((w.q[i, h].double() * k[g, 0]).sum()) * w.scale
+            assert abs(lse[i, h] - (s + math.log(len(keys)))) < 1e-12
+
+
+def test_gqa_group_shares_one_kv_head(oracle_lib):
+    rng = np.random.default_rng(11)
+    w = small([W.random_tree(rng, 20)], [40], hq=8, hkv=2, seed=11)
+    w.q[:, 1:4] = w.q[:, 0:1]                  # heads 0..3 = group 0
+    w.q[:, 5:8] = w.q[:, 4:5]                  # heads 4..7 = group 1
+    out, lse = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_len,
+                                w.cu_nodes, w.parent, 8, 2, w.scale)
+    for h in (1, 2, 3):
+        np.testing.assert_array_equal(out[:, h], out[:, 0])
+    for h in (5, 6, 7):
+        np.testing.assert_array_equal(out[:, h], out[:, 4])
+    assert np.abs(out[:, 0] - out[:, 4]).max() > 1e-3   # the two groups differ
+
+
+def test_non_ancestor_kv_does_not_matter(oracle_lib):
+    tree = [-1, 0, 0, 1, 1, 2, 2, 3]
+    P = 20
+    w = small([tree], [P], seed=5)
+    base, _ = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_len,
+                               w.cu_nodes, w.parent, 8, 2, w.scale)
+    R = closure(tree)
+    j = 2                                       # perturb node 2's K and V
+    pos = P + j
+    page, slot = w.block_table[0, pos // 16], pos % 16
+    w.k_cache[page, :, slot] += 3.0
+    w.v_cache[page, :, slot] -= 2.0
+    out, _ = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_len,
+                              w.cu_nodes, w.parent, 8, 2, w.scale)
+    for i in range(len(tree)):
+        if R[i, j]:
+            assert np.abs(out[i] - base[i]).max() > 1e-6
+        else:
+            np.testing.assert_array_equal(out[i], base[i])
+
+
+def test_page_permutation_and_row_subset_do_not_change_results(oracle_lib):
+    rng = np.random.default_rng(9)
+    tree = W.random_tree(rng, 33)
+    a = small([tree], [75], seed=9)
+    b = small([tree], [75], seed=9, permute_pages=True)
+    # same values, different placement: move b's pages so logical content matches a
+    for blk in range(a.block_table.shape[1]):
+        b.k_cache[b.block_table[0, blk]] = a.k_cache[a.block_table[0, blk]]
+        b.v_cache[b.block_table[0, blk]] = a.v_cache[a.block_table[0, blk]]
+    b.q.copy_(a.q)
+    oa, la = oracle.tree_attn(a.q, a.k_cache, a.v_cache, a.block_table, a.prefix_len,
+                              a.cu_nodes, a.parent, 8, 2, a.scale)
+    ob, lb = oracle.tree_attn(b.q, b.k_cache, b.v_cache, b.block_table, b.prefix_len,
+                              b.cu_nodes, b.parent, 8, 2, b.scale)
+    np.testing.assert_array_equal(oa, ob)
+    np.testing.assert_array_equal(la, lb)
+    rows = np.array([[0, 0], [32, 7], [5, 3]], np.int32)
+    orow, lrow = oracle.tree_attn(a.q, a.k_cache, a.v_cache, a.block_table, a.prefix_len,
+                                  a.cu_nodes, a.parent, 8, 2, a.scale, rows=rows)
+    for r, (i, h) in enumerate(rows):
+        np.testing.assert_array_equal(orow[r], oa[i, h])
+        assert lrow[r] == la[i, h]
+
+
+# ------------------------------------------------------------- acceptance --
+
+def chain_case(correct, seed=0):
+    """Root + len(correct) drafted nodes; drafted token k is right iff correct[k-1]."""
+    rng = np.random.default_rng(seed)
+    n = len(correct) + 1
+    par = [-1] + list(range(n - 1))
+    draft = rng.integers(1000, size=n).astype(np.int32)
+    target = rng.integers(1000, size=n).astype(np.int32)
+    for k in range(1, n):
+        target[k - 1] = draft[k] if correct[k - 1] else (draft[k] + 1) % 1000
+    return par, draft, target
+
+
+def test_specopd_illustration_golden(oracle_lib):
+    with open(os.path.join(GOLDEN, "specopd_al_illustration.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        par, dr, tg = chain_case(case["token_correct"])
+        al, path, bonus = oracle.accept(par, dr, tg, [0, len(par)], len(par) - 1)
+        assert al[0] == case["acceptance_length"], case["name"]
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_chain_acceptance_is_prefix_survival(oracle_lib, seed):
+    # BlockPilot §八: accepted length = sum_k prod_{j<=k} alpha_j; with the 0/1
+    # outcome of each position this is the index of the first mismatch.
+    rng = np.random.default_rng(seed)
+    correct = (rng.random(int(rng.integers(1, 25))) < 0.8)
+    par, dr, tg = chain_case(correct, seed)
+    al, path, bonus = oracle.accept(par, dr, tg, [0, len(par)], len(par) - 1)
+    survival = sum(np.prod(correct[:k + 1].astype(int)) for k in range(len(correct)))
+    first_miss = int(np.argmin(np.append(correct, False)))
+    assert al[0] == survival == first_miss
+    assert path[0, :al[0] + 1].tolist() == list(range(al[0] + 1))
+    assert (path[0, al[0] + 1:] == -1).all()
+    assert bonus[0] == tg[al[0]]
+
+
+def greedy_descent(par, dr, tg):
+    ch = [[] for _ in par]
+    for i in range(1, len(par)):
+        ch[par[i]].append(i)
+    cur, path = 0, [0]
+    while True:
+        nxt = [c for c in ch[cur] if dr[c] == tg[cur]]
+        if not nxt:
+            return path, tg[cur]
+        cur = nxt[0]
+        path.append(cur)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_distinct_siblings_acceptance_equals_greedy_descent(oracle_lib, seed):
+    w = W.build_workload("acc", [W.random_tree(np.random.default_rng(seed), int(n))
+                                 for n in (1, 9, 60, 200)],
+                         [0, 0, 0, 0], 2, 1, 8, "f32", seed, vocab=50, match_p=0.8)
+    md = w.max_depth
+    al, path, bonus = oracle.accept(w.parent, w.draft_tok, w.target_tok, w.cu_nodes, md)
+    for b in range(w.batch):
+        sl = slice(w.cu_nodes[b], w.cu_nodes[b + 1])
+        gp, gb = greedy_descent(w.parent[sl], w.draft_tok[sl], w.target_tok[sl])
+        assert al[b] == len(gp) - 1
+        assert path[b, :len(gp)].tolist() == gp
+        assert bonus[b] == gb
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_appending_nodes_never_shortens_acceptance(oracle_lib, seed):
+    # Graft §三: a superset tree never has a shorter longest accepted prefix.
+    rng = np.random.default_rng(seed)
+    par = W.random_tree(rng, 30)
+    dr = list(rng.integers(6, size=30))
+    tg = list(rng.integers(6, size=30))
+    prev = oracle.accept(par, dr, tg, [0, len(par)], 200)[0][0]
+    for _ in range(40):
+        par.append(int(rng.integers(len(par))))
+        dr.append(int(rng.integers(6)))
+        tg.append(int(rng.integers(6)))
+        cur = oracle.accept(par, dr, tg, [0, len(par)], 200)[0][0]
+        assert cur >= prev
+        prev = cur
+
+
+def test_repeated_sibling_tokens_pick_deepest_then_smallest_index(oracle_lib):
+    # root -> {1, 2} both carry token 7 and both match; 2 has an accepted child.
+    par = [-1, 0, 0, 2, 1]
+    dr = [0, 7, 7, 9, 9]
+    tg = [7, 9, 9, 0, 0]
+    al, path, bonus = oracle.accept(par, dr, tg, [0, 5], 4)
+    assert al[0] == 2 and path[0, :3].tolist() == [0, 2, 3]   # 3 (via 2) ties 4 (via 1): smaller index
+    assert bonus[0] == tg[3]
+    par2 = [-1, 0, 0, 2]
+    dr2 = [0, 7, 7, 9]
+    tg2 = [7, 0, 9, 0]
+    al2, path2, _ = oracle.accept(par2, dr2, tg2, [0, 4], 3)
+    assert al2[0] == 2 and path2[0, :3].tolist() == [0, 2, 3]

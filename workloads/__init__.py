@@ -1,0 +1,16 @@
+"""Seeded synthetic workloads for tree-verification attention.
+
+This package only draws inputs (trees, token ids, Q/K/V, page tables).  It
+holds none of the arithmetic of the verification path (no mask building, no
+attention, no acceptance), so both the HIP path and the CPU oracle can take
+their inputs from it.
+"""
+from .configs import (  # noqa: F401
+    Workload,
+    CONFIG_NAMES,
+    GRAFT_TREE_PARENT,
+    build_workload,
+    make,
+    random_tree,
+    trunk_branch_tree,
+)
