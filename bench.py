@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of one tree-verification step on one MI355X.
+
+A step is the whole hot path over one batch: tree_mask_build ->
+tree_verify_attn -> tree_accept. The default workload is the Graft-shaped
+60-node tree (batch 1, 2048-token prefix, Qwen3-8B attention: 32 query / 8 kv
+heads, head_dim 128, bf16, 16-token pages). Inputs are seeded synthetic data
+resident in HBM; R copies of Q/K/V are rotated so that consecutive steps do
+not find their KV in the 256 MB last-level cache. The K timed steps are
+replayed from a HIP graph captured from the library's own launches.
+
+Prints one JSON line: throughput in verified tree-tokens/s, the attention
+kernel's achieved HBM bandwidth against the 8 TB/s peak (HIP events over the
+timed region), and the CPU oracle's rate on the host as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verified tree-tokens/s and achieved HBM TB/s (% of peak), Qwen3-8B-shaped 60-node tree"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+VALU_FP32_PEAK_TFLOPS = 157.3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def depths(parent, cu):
+    d = [0] * len(parent)
+    for b in range(len(cu) - 1):
+        for i in range(int(cu[b]) + 1, int(cu[b + 1])):
+            d[i] = d[int(cu[b]) + int(parent[i])] + 1
+    return d
+
+
+def algorithmic_work(w):
+    """Bytes: Q read once, every prefix and tree K/V row read once, O written
+    once. FLOPs: 4 * head_dim per visible (row, key) pair (QK^T and PV)."""
+    import numpy as np
+    elt = 2 if w.dtype == "bf16" else 4
+    n, hq, hkv, d = w.total_nodes, w.num_q_heads, w.num_kv_heads, w.head_dim
+    kv_rows = int(np.sum(w.prefix_len.astype(np.int64) + w.nodes_per_request))
+    bytes_ = 2 * n * hq * d * elt + 2 * kv_rows * hkv * d * elt
+    dep = depths(w.parent, w.cu_nodes)
+    pairs = 0
+    for b in range(w.batch):
+        for i in range(int(w.cu_nodes[b]), int(w.cu_nodes[b + 1])):
+            pairs += int(w.prefix_len[b]) + dep[i] + 1
+    flops = 4 * d * hq * pairs
+    return bytes_, flops
+
+
+def cpu_baseline(w, seconds):
+    """The oracle, as it is, over whole steps of the same workload, single thread."""
+    import numpy as np
+    import oracle
+    q = w.q.float().numpy()
+    k = w.k_cache.float().numpy()
+    v = w.v_cache.float().numpy()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        if w.mask_kind == "bits":
+            oracle.mask_bits(w.parent, w.cu_nodes, w.words_per_node)
+        else:
+            oracle.mask_anchor(w.parent, w.cu_nodes)
+        oracle.tree_attn(q, k, v, w.block_table, w.prefix_len, w.cu_nodes, w.parent,
+                         w.num_q_heads, w.num_kv_heads, w.scale)
+        if w.draft_tok is not None:
+            oracle.accept(w.parent, w.draft_tok, w.target_tok, w.cu_nodes, w.max_depth)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    del q, k, v, np
+    return {"value": reps * w.total_nodes / el, "unit": "tree-tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d whole steps of %s (mask + fp64 attention over all %d x %d rows + "
+                      "acceptance) in %.1f s, one thread" % (reps, w.name, w.total_nodes,
+                                                             w.num_q_heads, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2, the headline)")
+    ap.add_argument("--rot", type=int, default=0, help="rotating buffer sets (0 = auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode (requests, kv-head "
+              "groups or key ranges would shard with no exchange but one LSE merge). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import tree_verification_attention_mask_amd as tv
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    w = W.make(args.config)
+    log("workload", w.name, "nodes", w.total_nodes, "max prefix", w.max_prefix_len)
+    alg_bytes, alg_flops = algorithmic_work(w)
+    kv_bytes = 2 * w.k_cache.numel() * w.k_cache.element_size()
+    set_bytes = kv_bytes + 2 * w.q.numel() * w.q.element_size()
+    R = args.rot or max(1, min(64, math.ceil(512e6 / set_bytes)))
+
+    parent = torch.from_numpy(w.parent).to(dev)
+    cu = torch.from_numpy(w.cu_nodes).to(dev)
+    prefix = torch.from_numpy(w.prefix_len).to(dev)
+    table = torch.from_numpy(w.block_table).to(dev)
+    has_tok = w.draft_tok is not None
+    draft = torch.from_numpy(w.draft_tok).to(dev) if has_tok else None
+    target = torch.from_numpy(w.target_tok).to(dev) if has_tok else None
+    q0, k0, v0 = w.q.to(dev), w.k_cache.to(dev), w.v_cache.to(dev)
+    qs = [q0] + [q0.clone() for _ in range(R - 1)]
+    ks = [k0] + [k0.clone() for _ in range(R - 1)]
+    vs = [v0] + [v0.clone() for _ in range(R - 1)]
+    outs = [torch.empty_like(q0) for _ in range(R)]
+    lses = [torch.empty(q0.shape[:2], dtype=torch.float32, device=dev) for _ in range(R)]
+    need = tv.verify_attn_workspace_size(w.batch, w.total_nodes, w.max_nodes, w.max_prefix_len,
+                                         w.num_q_heads, w.num_kv_heads, w.head_dim, q0.dtype)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    mask_out = {}
+    acc_out = {}
+    m = tv.tree_mask_build(parent, cu, w.max_nodes, kind=w.mask_kind)
+    mask_out = {k_: v_ for k_, v_ in m.items() if isinstance(v_, torch.Tensor)}
+    if has_tok:
+        al, path, bonus = tv.tree_accept(parent, draft, target, cu, w.max_nodes, w.max_depth)
+        acc_out = {"accept_len": al, "path": path, "bonus": bonus}
+
+    def mask_call():
+        return tv.tree_mask_build(parent, cu, w.max_nodes, kind=w.mask_kind, out=mask_out)
+
+    def attn_call(s, mk):
+        tv.tree_verify_attn(qs[s], ks[s], vs[s], table, prefix, cu, mk, w.max_nodes,
+                            w.max_prefix_len, scale=w.scale, out=outs[s], lse=lses[s],
+                            workspace=ws)
+
+    def accept_call():
+        if has_tok:
+            tv.tree_accept(parent, draft, target, cu, w.max_nodes, w.max_depth, out=acc_out)
+
+    def step(s):
+        mk = mask_call()
+        attn_call(s, mk)
+        accept_call()
+
+    for i in range(args.warmup):
+        step(i % R)
+    torch.cuda.synchronize()
+    eager_out = outs[0].clone()
+    eager_acc = [t.clone() for t in acc_out.values()]
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    g_full = capture(lambda: [step(s) for s in range(R)])
+    rem = args.steps % R
+    g_rem = capture(lambda: [step(s) for s in range(rem)]) if rem else None
+    g_attn = capture(lambda: [attn_call(s, mask_out | {"kind": w.mask_kind,
+                                                      "words_per_node": m["words_per_node"]})
+                              for s in range(R)])
+    g_mask = capture(lambda: [mask_call() for _ in range(R)])
+    g_acc = capture(lambda: [accept_call() for _ in range(R)]) if has_tok else None
+    # a replay reproduces the eager results bit for bit
+    outs[0].zero_()
+    g_full.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], eager_out), "graph replay differs from eager run"
+    assert all(torch.equal(a, b) for a, b in zip(acc_out.values(), eager_acc))
+
+    reps_full = args.steps // R
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record()
+    for _ in range(reps_full):
+        g_full.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    log("timed %d steps: %.3f ms (events), %.3f s wall" % (args.steps, ms_total, wall))
+
+    def time_graph(g, calls_per_replay):
+        reps = max(1, args.steps // R)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g.replay()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (reps * calls_per_replay)  # us per call
+
+    us_attn = time_graph(g_attn, R)
+    us_mask = time_graph(g_mask, R)
+    us_acc = time_graph(g_acc, R) if g_acc is not None else 0.0
+    achieved_gbs = alg_bytes / (us_attn * 1e-6) / 1e9
+    achieved_tflops = alg_flops / (us_attn * 1e-6) / 1e12
+    plan_splits = (need > 0)
+
+    result = {
+        "metric": METRIC,
+        "value": w.total_nodes / (ms_per_step * 1e-3),
+        "unit": "tree-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) Q/K/V, generated tree and tokens)",
+        "config": {"workload": w.name, "batch": w.batch, "tree_nodes": w.total_nodes,
+                   "max_prefix_len": w.max_prefix_len, "q_heads": w.num_q_heads,
+                   "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
+                   "mask": w.mask_kind, "rotating_buffer_sets": R, "hip_graph": True},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "tree_verify_attn (attn_bf16_kernel%s)" %
+                               (" + combine_kernel" if plan_splits else ""),
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "us_per_launch": us_attn},
+        "mfma": {"achieved_tflops": achieved_tflops, "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                 "frac": achieved_tflops / MFMA_BF16_PEAK_TFLOPS,
+                 "algorithmic_flops_per_launch": alg_flops},
+        "breakdown_us": {"tree_mask_build": us_mask, "tree_verify_attn": us_attn,
+                         "tree_accept": us_acc, "step": ms_per_step * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle (about %.0f s)" % args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+/*
+ * treeverify.h -- C ABI of the MI355X (gfx950) tree-verification library.
+ *
+ * One speculative-decoding verification step over a flattened candidate tree:
+ *   1. tv_tree_mask_build  parent[] -> depth and the ancestor-only tree mask
+ *   2. tv_tree_verify_attn one target attention layer: every tree node attends
+ *                          the request's KV prefix plus its own root path
+ *   3. tv_tree_accept      greedy acceptance: longest accepted root-to-leaf path
+ *
+ * Sources (four web pages on candidate-tree speculative decoding):
+ *   Graft      arXiv:2605.20104 -- 163.com article "浙江大学、阿里巴巴联手破解AI推理瓶颈"
+ *   BlockPilot arXiv:2606.31315 -- zhengruan.com article on dynamic block size
+ *   D-cut      paper 2607.14647 -- gist.science summary "D-cut: Adaptive Verification
+ *              Depth Pruning for Batched Speculative Decoding"
+ *   SpecOPD    arXiv:2611.02846 -- lewlh.github.io blog post on branch-parallel OPD
+ *
+ * Conventions (all calls):
+ *   - Every pointer is a DEVICE pointer unless its comment says (host).
+ *   - The caller allocates and owns every buffer, including the workspace.
+ *     The library never allocates, frees or synchronises; each call only
+ *     enqueues kernels on `stream` and returns. Results are ready when the
+ *     stream reaches that point.
+ *   - Trees are packed ragged: request b owns flattened nodes
+ *     [cu_nodes[b], cu_nodes[b+1]). parent[] holds REQUEST-LOCAL indices in
+ *     topological order: the root is local node 0 with parent -1 and every
+ *     other node i has 0 <= parent[i] < i.
+ *   - Shape scalars that size a launch (batch, total_nodes, max_nodes,
+ *     max_prefix_len, max_depth) come from the host, so no call reads device
+ *     memory back. They must be >= the true values in the device arrays;
+ *     if they are not, results are undefined but no access leaves the
+ *     buffers described below.
+ *   - Returns TV_OK once the work is enqueued, or an error status before
+ *     enqueueing anything (bad arguments) / after a failed launch (TV_ERR_HIP).
+ *   - Deterministic: the launch plan depends only on host scalars and every
+ *     reduction has a fixed order, so repeated calls give identical bits.
+ */
+#ifndef TREEVERIFY_H
+#define TREEVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TV_OK = 0,
+  TV_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, inconsistent shape */
+  TV_ERR_UNSUPPORTED = 2,      /* valid but outside what the kernels implement */
+  TV_ERR_WORKSPACE = 3,        /* workspace_bytes below tv_tree_verify_attn_workspace_size */
+  TV_ERR_HIP = 4               /* a HIP launch failed */
+} tv_status_t;
+
+typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype_t;
+
+typedef enum {
+  TV_MASK_BITS = 0,   /* ancestor bitmask, words_per_node 64-bit words per node */
+  TV_MASK_ANCHOR = 1  /* anchor position + branch depth (trunk plus chain branches) */
+} tv_mask_kind_t;
+
+/* Per-node limits. */
+#define TV_MAX_MASK_WORDS 16          /* BITS form: up to 1024 nodes per request */
+#define TV_MAX_ACCEPT_NODES 8192      /* tv_tree_accept: nodes per request */
+
+/*
+ * Tree mask, as tv_tree_verify_attn reads it (a host struct of device pointers).
+ * BITS:   bits[node * words_per_node + j / 64] bit (j % 64) set  <=>  local tree
+ *         node j is node's ancestor or node itself.
+ * ANCHOR: local tree key j is visible to local node i  <=>
+ *         j <= anchor_pos[i]  or  i - branch_depth[i] < j <= i.
+ * Prefix keys (positions < prefix_len[b]) are visible to every node of the
+ * request in both forms; only the tree-to-tree block is masked.
+ */
+typedef struct {
+  int32_t kind;                /* tv_mask_kind_t */
+  int32_t words_per_node;      /* BITS only: 1 .. TV_MAX_MASK_WORDS */
+  const uint64_t* bits;        /* BITS:   [total_nodes][words_per_node] */
+  const int32_t* anchor_pos;   /* ANCHOR: [total_nodes] */
+  const int32_t* branch_depth; /* ANCHOR: [total_nodes] */
+} tv_mask_t;
+
+/*
+ * tv_tree_mask_build -- tree positions and the ancestor-only tree mask.
+ *
+ * Graft §二 (third gear): the hybrid tree of draft and retrieved nodes is
+ * flattened into a sequence and its tree position ids and tree mask are
+ * rebuilt before one parallel verification pass. SpecOPD §02 (attention
+ * table, full-attention/GQA row): the mask is the topological ancestor
+ * relation -- a node sees its own ancestor path and the shared trunk, not its
+ * siblings' branches nor later trunk tokens. The position id of node i is
+ * prefix_len + depth[i].
+ *
+ *   parent        [total_nodes]  request-local parent indices (see conventions)
+ *   cu_nodes      [batch + 1]    node offsets; cu_nodes[0] = 0
+ *   batch         (host) number of requests, >= 1
+ *   total_nodes   (host) cu_nodes[batch]
+ *   max_nodes     (host) >= every request's node count
+ *   kind          TV_MASK_BITS or TV_MASK_ANCHOR
+ *   words_per_node BITS: 64-bit words per node, ceil(max_nodes/64) <= value <= 16
+ *   bits          BITS:   out [total_nodes][words_per_node]
+ *   anchor_pos    ANCHOR: out [total_nodes]  last visible trunk index (node itself on the trunk)
+ *   branch_depth  ANCHOR: out [total_nodes]  1-based depth inside its branch, 0 on the trunk.
+ *                 The trunk is the longest prefix 0..T-1 with parent[k] = k-1; every later
+ *                 node must start a branch (parent < T) or continue the previous node's
+ *                 branch (parent = i-1).
+ *   depth         out [total_nodes]  number of ancestors (root 0)
+ *   err           out [batch]  0 = ok; 1 = malformed parent[] (parent[0] != -1, or a
+ *                 parent outside [0, i)) or, BITS, more nodes than words_per_node*64;
+ *                 2 = ANCHOR form impossible for this tree. A request with err != 0 gets
+ *                 an all-zero mask (ANCHOR: anchor_pos -1, branch_depth 0) and depth -1.
+ * Unused outputs of the other form may be NULL.
+ */
+tv_status_t tv_tree_mask_build(const int32_t* parent, const int32_t* cu_nodes, int32_t batch,
+                               int32_t total_nodes, int32_t max_nodes, int32_t kind,
+                               int32_t words_per_node, uint64_t* bits, int32_t* anchor_pos,
+                               int32_t* branch_depth, int32_t* depth, int32_t* err,
+                               hipStream_t stream);
+
+/*
+ * Workspace bytes tv_tree_verify_attn needs for these host shape scalars
+ * (split-KV partial results). 0 means no workspace is needed.
+ */
+size_t tv_tree_verify_attn_workspace_size(int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                                          int32_t max_prefix_len, int32_t num_q_heads,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t dtype);
+
+/*
+ * tv_tree_verify_attn -- one target attention layer over the flattened tree.
+ *
+ * Graft §二 (third gear): one parallel verification pass of the target over
+ * the flattened tree under the tree mask. SpecOPD §02 (proposal tree): the
+ * target shares the trunk KV cache and scores every branch in one pass under
+ * the tree mask. D-cut technical summary §2 (pipeline, packing/verification):
+ * the kept positions of every request form a contiguous prefix of its block
+ * and the packed batch is verified in one pass.
+ *
+ * For request b, tree node i (local) and query head h, with G = Hq/Hkv and
+ * kv head g = h / G, P = prefix_len[b], n = node count of b:
+ *   keys   = positions p in [0, P)  U  {P + j : j visible to i under `mask`}
+ *   s_p    = softmax_scale * <q[i,h,:], K[p,g,:]>
+ *   out    = sum_p softmax(s)_p V[p,g,:]        lse = ln sum_p exp(s_p)
+ * where K/V at logical position p of request b live in page
+ * block_table[b*max_pages_per_req + p/page_size], slot p % page_size.
+ * The tree nodes' own K/V are at positions P .. P+n-1 (written by the caller).
+ *
+ *   q            [total_nodes][num_q_heads][head_dim]            dtype
+ *   k_cache      [num_pages][num_kv_heads][page_size][head_dim]  dtype
+ *   v_cache      same layout as k_cache
+ *   num_pages    (host) pages in the caches; page ids are clamped into range
+ *   block_table  [batch][max_pages_per_req]  entries past a request's last page are not read
+ *   prefix_len   [batch]
+ *   cu_nodes     [batch + 1]
+ *   max_prefix_len (host) >= every prefix_len
+ *   head_dim     64 or 128;  num_q_heads % num_kv_heads == 0
+ *   page_size    multiple of 4 (16 in the measured configurations)
+ *   dtype        TV_BF16 (MFMA path) or TV_F32 (fp32 VALU path)
+ *   softmax_scale usually 1/sqrt(head_dim)
+ *   mask         (host) struct of device pointers, typically from tv_tree_mask_build
+ *                (ANCHOR needs every request in anchor form)
+ *   out          [total_nodes][num_q_heads][head_dim]  dtype (round to nearest even)
+ *   lse          [total_nodes][num_q_heads] fp32 natural log, or NULL
+ *   workspace    >= tv_tree_verify_attn_workspace_size(...) bytes, 256-byte aligned,
+ *                or NULL when that size is 0. Contents on entry are ignored.
+ * Calls that share a workspace must not overlap in time.
+ */
+tv_status_t tv_tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
+                                int32_t num_pages, const int32_t* block_table,
+                                int32_t max_pages_per_req, const int32_t* prefix_len,
+                                const int32_t* cu_nodes, int32_t batch, int32_t total_nodes,
+                                int32_t max_nodes, int32_t max_prefix_len, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                int32_t dtype, float softmax_scale, const tv_mask_t* mask,
+                                void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
+ * tv_tree_accept -- greedy acceptance of the longest matching root path.
+ *
+ * SpecOPD §01: drafted tokens that agree with the target are accepted, the
+ * draft is cut at the first divergence and the rest discarded. Graft
+ * introduction: the target checks the whole tree at once and keeps the path
+ * that goes furthest; Graft §二 (third gear): draft and retrieved nodes face
+ * the same rule. BlockPilot §八: accepted length is the survival length of
+ * the prefix.
+ *
+ * Node i > 0 matches iff draft_tok[i] == target_tok[parent[i]] (target_tok[v]
+ * is the target's greedy token after node v). A node is accepted iff all
+ * nodes on its root path match; the root is always accepted. best = accepted
+ * node of greatest depth, ties to the smallest local index.
+ *
+ *   parent, draft_tok, target_tok  [total_nodes]
+ *   cu_nodes     [batch + 1]
+ *   max_nodes    (host) >= every request's node count, <= TV_MAX_ACCEPT_NODES
+ *   max_depth    (host) path row length - 1
+ *   accept_len   out [batch]  depth of best = accepted non-root nodes
+ *   path         out [batch][max_depth + 1]  local node ids root..best, then -1;
+ *                entries past max_depth are not written
+ *   bonus_tok    out [batch]  target_tok[best] (the target's next token), or NULL
+ * parent[] must be a valid tree (tv_tree_mask_build reports it); on a malformed
+ * tree indices are clamped, results are undefined and nothing is read or
+ * written out of bounds.
+ */
+tv_status_t tv_tree_accept(const int32_t* parent, const int32_t* draft_tok,
+                           const int32_t* target_tok, const int32_t* cu_nodes, int32_t batch,
+                           int32_t total_nodes, int32_t max_nodes, int32_t max_depth,
+                           int32_t* accept_len, int32_t* path, int32_t* bonus_tok,
+                           hipStream_t stream);
+
+/* Static description of a status code. */
+const char* tv_status_string(tv_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TREEVERIFY_H */

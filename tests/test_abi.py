@@ -1,0 +1,97 @@
+"""The C-ABI library loads and exports every symbol ``include/treeverify.h``
+declares; host-side argument checks return the documented status codes before
+anything is launched (no GPU needed: only early-return paths are called)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tree_verification_attention_mask_amd as tv
+from tree_verification_attention_mask_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "treeverify.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below returns before a launch
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tv_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tv.load_library()
+    names = declared_functions()
+    assert names == sorted(binding.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = tv.load_library()
+    for code, text in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported configuration"),
+                       (3, b"workspace too small"), (4, b"HIP launch failed"),
+                       (99, b"unknown status")]:
+        assert lib.tv_status_string(code) == text
+
+
+def test_workspace_size_is_a_pure_host_query():
+    lib = tv.load_library()
+    ws = lib.tv_tree_verify_attn_workspace_size
+    assert ws(1, 60, 60, 64, 32, 8, 128, 1) == 0           # short prefix: one key split
+    big = ws(1, 60, 60, 2048, 32, 8, 128, 1)
+    assert big > 0 and big % 256 == 0
+    assert ws(1, 60, 60, 2048, 32, 8, 128, 0) == 0         # fp32 path never splits
+    assert ws(0, 60, 60, 2048, 32, 8, 128, 1) == 0         # invalid shape -> 0
+
+
+def _attn(lib, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, pages=10, table=FAKE, maxp=4, prefix=FAKE, cu=FAKE, batch=1,
+             total=60, maxn=60, maxP=2048, hq=32, hkv=8, d=128, page=16, dtype=1, scale=0.08,
+             out=FAKE, lse=None, ws=None, wsb=0)
+    a.update(over)
+    m = binding.Mask(0, 1, 0x1000, None, None)
+    return lib.tv_tree_verify_attn(a["q"], a["k"], a["v"], a["pages"], a["table"], a["maxp"],
+                                   a["prefix"], a["cu"], a["batch"], a["total"], a["maxn"],
+                                   a["maxP"], a["hq"], a["hkv"], a["d"], a["page"], a["dtype"],
+                                   ctypes.c_float(a["scale"]), ctypes.byref(m), a["out"],
+                                   a["lse"], a["ws"], a["wsb"], None)
+
+
+def test_attn_argument_checks():
+    lib = tv.load_library()
+    assert _attn(lib, q=None) == 1
+    assert _attn(lib, hq=30) == 1            # Hq not a multiple of Hkv
+    assert _attn(lib, dtype=7) == 1
+    assert _attn(lib, d=96) == 2
+    assert _attn(lib, page=6) == 2
+    assert _attn(lib, batch=0) == 1
+    assert _attn(lib, maxn=65) == 1          # one mask word cannot hold 65 nodes
+    assert _attn(lib) == 3                   # a 2048-key prefix needs split workspace
+    assert _attn(lib, ws=FAKE, wsb=16) == 3
+
+
+def test_mask_and_accept_argument_checks():
+    lib = tv.load_library()
+    mb = lib.tv_tree_mask_build
+    assert mb(None, FAKE, 1, 4, 4, 0, 1, FAKE, None, None, FAKE, FAKE, None) == 1
+    assert mb(FAKE, FAKE, 1, 4, 4, 0, 17, FAKE, None, None, FAKE, FAKE, None) == 2
+    assert mb(FAKE, FAKE, 1, 2000, 2000, 0, 16, FAKE, None, None, FAKE, FAKE, None) == 2
+    assert mb(FAKE, FAKE, 1, 100, 100, 0, 1, FAKE, None, None, FAKE, FAKE, None) == 1
+    assert mb(FAKE, FAKE, 1, 4, 4, 1, 0, None, None, None, FAKE, FAKE, None) == 1
+    assert mb(FAKE, FAKE, 1, 4, 4, 5, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    ac = lib.tv_tree_accept
+    assert ac(None, FAKE, FAKE, FAKE, 1, 4, 4, 3, FAKE, FAKE, None, None) == 1
+    assert ac(FAKE, FAKE, FAKE, FAKE, 1, 4, 4, -1, FAKE, FAKE, None, None) == 1
+    assert ac(FAKE, FAKE, FAKE, FAKE, 1, 9000, 9000, 3, FAKE, FAKE, None, None) == 2
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "tree_verification_attention_mask_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower().replace("oracle-free", ""), f

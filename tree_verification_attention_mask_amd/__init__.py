@@ -1,0 +1,17 @@
+"""MI355X (gfx950) tree-verification attention: mask build, verify attention, greedy accept.
+
+The three calls are thin wrappers over the C ABI of ``lib/libtreeverify.so``
+(``include/treeverify.h``); build it with
+``python -m tree_verification_attention_mask_amd.build``.
+"""
+from .binding import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    TVError,
+    load_library,
+    mask_struct,
+    tree_accept,
+    tree_mask_build,
+    tree_verify_attn,
+    verify_attn_workspace_size,
+)

@@ -1,0 +1,197 @@
+"""Thin ctypes binding of ``libtreeverify.so`` (C ABI in ``include/treeverify.h``).
+
+Argument marshalling only: tensors become device pointers, host scalars are
+passed through, outputs are allocated with torch when the caller does not
+supply them, and every call is enqueued on torch's current HIP stream.  All
+computation happens in the library's kernels.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libtreeverify.so")
+
+TV_OK, TV_ERR_INVALID_ARGUMENT, TV_ERR_UNSUPPORTED, TV_ERR_WORKSPACE, TV_ERR_HIP = range(5)
+TV_F32, TV_BF16 = 0, 1
+TV_MASK_BITS, TV_MASK_ANCHOR = 0, 1
+MAX_MASK_WORDS = 16
+MAX_ACCEPT_NODES = 8192
+
+# every symbol the header declares
+EXPORTS = ("tv_tree_mask_build", "tv_tree_verify_attn_workspace_size", "tv_tree_verify_attn",
+           "tv_tree_accept", "tv_status_string")
+
+
+class TVError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__("%s failed: status %d (%s)" % (fn, status, msg))
+        self.status = status
+
+
+class Mask(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("words_per_node", ctypes.c_int32),
+                ("bits", ctypes.c_void_p), ("anchor_pos", ctypes.c_void_p),
+                ("branch_depth", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError("libtreeverify.so not found at %s -- build it with "
+                          "`python -m tree_verification_attention_mask_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    P, I, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.tv_tree_mask_build.argtypes = [P, P, I, I, I, I, I, P, P, P, P, P, P]
+    lib.tv_tree_mask_build.restype = ctypes.c_int
+    lib.tv_tree_verify_attn_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
+    lib.tv_tree_verify_attn_workspace_size.restype = S
+    lib.tv_tree_verify_attn.argtypes = [P, P, P, I, P, I, P, P, I, I, I, I, I, I, I, I, I,
+                                        ctypes.c_float, ctypes.POINTER(Mask), P, P, P, S, P]
+    lib.tv_tree_verify_attn.restype = ctypes.c_int
+    lib.tv_tree_accept.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P]
+    lib.tv_tree_accept.restype = ctypes.c_int
+    lib.tv_status_string.argtypes = [ctypes.c_int]
+    lib.tv_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != TV_OK:
+        raise TVError(fn, status, load_library().tv_status_string(status).decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dev_i32(x, device):
+    if isinstance(x, torch.Tensor):
+        assert x.dtype == torch.int32 and x.is_contiguous() and x.device.type == "cuda"
+        return x
+    return torch.as_tensor(x, dtype=torch.int32, device=device).contiguous()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def tree_mask_build(parent: torch.Tensor, cu_nodes: torch.Tensor, max_nodes: int,
+                    kind: str = "bits", words_per_node: int | None = None, out: dict | None = None,
+                    stream=None) -> dict:
+    """Depth and ancestor mask of every node (``tv_tree_mask_build``).
+
+    Returns a dict with ``kind``, ``depth``, ``err`` and either ``bits``
+    (uint64 as int64 [N, words]) or ``anchor_pos`` / ``branch_depth``.
+    """
+    lib = load_library()
+    dev = parent.device
+    batch = cu_nodes.numel() - 1
+    n = parent.numel()
+    k = TV_MASK_BITS if kind == "bits" else TV_MASK_ANCHOR
+    words = words_per_node if words_per_node is not None else max(1, (max_nodes + 63) // 64)
+    o = dict(out or {})
+    o.setdefault("depth", torch.empty(n, dtype=torch.int32, device=dev))
+    o.setdefault("err", torch.empty(batch, dtype=torch.int32, device=dev))
+    if k == TV_MASK_BITS:
+        o.setdefault("bits", torch.empty((n, words), dtype=torch.int64, device=dev))
+    else:
+        o.setdefault("anchor_pos", torch.empty(n, dtype=torch.int32, device=dev))
+        o.setdefault("branch_depth", torch.empty(n, dtype=torch.int32, device=dev))
+    st = lib.tv_tree_mask_build(_ptr(parent), _ptr(cu_nodes), batch, n, int(max_nodes), k,
+                                words if k == TV_MASK_BITS else 0, _ptr(o.get("bits")),
+                                _ptr(o.get("anchor_pos")), _ptr(o.get("branch_depth")),
+                                _ptr(o["depth"]), _ptr(o["err"]), _stream(stream))
+    _check("tv_tree_mask_build", st)
+    o["kind"] = kind
+    o["words_per_node"] = words if k == TV_MASK_BITS else 0
+    return o
+
+
+def mask_struct(mask: dict) -> Mask:
+    if mask["kind"] == "bits":
+        return Mask(TV_MASK_BITS, int(mask["words_per_node"]), mask["bits"].data_ptr(), None, None)
+    return Mask(TV_MASK_ANCHOR, 0, None, mask["anchor_pos"].data_ptr(),
+                mask["branch_depth"].data_ptr())
+
+
+def verify_attn_workspace_size(batch: int, total_nodes: int, max_nodes: int, max_prefix_len: int,
+                               num_q_heads: int, num_kv_heads: int, head_dim: int,
+                               dtype: torch.dtype) -> int:
+    lib = load_library()
+    dt = TV_F32 if dtype == torch.float32 else TV_BF16
+    return int(lib.tv_tree_verify_attn_workspace_size(batch, total_nodes, max_nodes, max_prefix_len,
+                                                      num_q_heads, num_kv_heads, head_dim, dt))
+
+
+def tree_verify_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                     block_table: torch.Tensor, prefix_len: torch.Tensor, cu_nodes: torch.Tensor,
+                     mask: dict, max_nodes: int, max_prefix_len: int, scale: float | None = None,
+                     out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True,
+                     workspace: torch.Tensor | None = None, stream=None):
+    """One tree-verification attention layer (``tv_tree_verify_attn``).
+
+    ``q`` [N, Hq, D]; caches [pages, Hkv, page, D] (bf16 or fp32);
+    ``block_table`` int32 [B, max_pages]; returns (out [N, Hq, D], lse [N, Hq] or None).
+    """
+    lib = load_library()
+    n, hq, d = q.shape
+    pages, hkv, page, d2 = k_cache.shape
+    assert d2 == d and v_cache.shape == k_cache.shape
+    assert q.dtype == k_cache.dtype == v_cache.dtype and q.is_contiguous()
+    assert k_cache.is_contiguous() and v_cache.is_contiguous() and block_table.is_contiguous()
+    batch = cu_nodes.numel() - 1
+    dt = TV_F32 if q.dtype == torch.float32 else TV_BF16
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is True:
+        lse = torch.empty((n, hq), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    need = int(lib.tv_tree_verify_attn_workspace_size(batch, n, int(max_nodes), int(max_prefix_len),
+                                                      hq, hkv, d, dt))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ms = mask_struct(mask)
+    if scale is None:
+        scale = d ** -0.5
+    st = lib.tv_tree_verify_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), pages, _ptr(block_table),
+                                 block_table.shape[1], _ptr(prefix_len), _ptr(cu_nodes), batch, n,
+                                 int(max_nodes), int(max_prefix_len), hq, hkv, d, page, dt,
+                                 float(scale), ctypes.byref(ms), _ptr(out), _ptr(lse),
+                                 _ptr(workspace), ws_bytes, _stream(stream))
+    _check("tv_tree_verify_attn", st)
+    return out, lse
+
+
+def tree_accept(parent: torch.Tensor, draft_tok: torch.Tensor, target_tok: torch.Tensor,
+                cu_nodes: torch.Tensor, max_nodes: int, max_depth: int, out: dict | None = None,
+                stream=None):
+    """Greedy acceptance (``tv_tree_accept``): returns (accept_len [B], path [B, max_depth+1], bonus [B])."""
+    lib = load_library()
+    dev = parent.device
+    batch = cu_nodes.numel() - 1
+    o = dict(out or {})
+    o.setdefault("accept_len", torch.empty(batch, dtype=torch.int32, device=dev))
+    o.setdefault("path", torch.empty((batch, max_depth + 1), dtype=torch.int32, device=dev))
+    o.setdefault("bonus", torch.empty(batch, dtype=torch.int32, device=dev))
+    st = lib.tv_tree_accept(_ptr(parent), _ptr(draft_tok), _ptr(target_tok), _ptr(cu_nodes), batch,
+                            parent.numel(), int(max_nodes), int(max_depth), _ptr(o["accept_len"]),
+                            _ptr(o["path"]), _ptr(o["bonus"]), _stream(stream))
+    _check("tv_tree_accept", st)
+    return o["accept_len"], o["path"], o["bonus"]

@@ -1,0 +1,133 @@
+// tv_api.hip -- the library's C ABI: host-side argument checks, launch plans,
+// kernel launches. Nothing here allocates, frees or synchronises.
+#include <algorithm>
+
+#include "tv_internal.h"
+
+using namespace tv;
+
+namespace {
+inline tv_status_t launched(hipError_t e) { return e == hipSuccess ? TV_OK : TV_ERR_HIP; }
+}  // namespace
+
+extern "C" const char* tv_status_string(tv_status_t s) {
+  switch (s) {
+    case TV_OK: return "ok";
+    case TV_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case TV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TV_ERR_WORKSPACE: return "workspace too small";
+    case TV_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+extern "C" tv_status_t tv_tree_mask_build(const int32_t* parent, const int32_t* cu_nodes,
+                                          int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                                          int32_t kind, int32_t words_per_node, uint64_t* bits,
+                                          int32_t* anchor_pos, int32_t* branch_depth,
+                                          int32_t* depth, int32_t* err, hipStream_t stream) {
+  if (!parent || !cu_nodes || !depth || !err) return TV_ERR_INVALID_ARGUMENT;
+  if (batch < 1 || total_nodes < 0 || max_nodes < 1) return TV_ERR_INVALID_ARGUMENT;
+  if (kind == TV_MASK_BITS) {
+    if (!bits) return TV_ERR_INVALID_ARGUMENT;
+    if (max_nodes > 64 * TV_MAX_MASK_WORDS || words_per_node > TV_MAX_MASK_WORDS)
+      return TV_ERR_UNSUPPORTED;
+    if (words_per_node < 1 || (int64_t)words_per_node * 64 < max_nodes) return TV_ERR_INVALID_ARGUMENT;
+    return launched(launch_mask_bits(parent, cu_nodes, batch, total_nodes, words_per_node, bits,
+                                     depth, err, stream));
+  }
+  if (kind == TV_MASK_ANCHOR) {
+    if (!anchor_pos || !branch_depth) return TV_ERR_INVALID_ARGUMENT;
+    return launched(launch_mask_anchor(parent, cu_nodes, batch, total_nodes, anchor_pos,
+                                       branch_depth, depth, err, stream));
+  }
+  return TV_ERR_INVALID_ARGUMENT;
+}
+
+extern "C" size_t tv_tree_verify_attn_workspace_size(int32_t batch, int32_t total_nodes,
+                                                     int32_t max_nodes, int32_t max_prefix_len,
+                                                     int32_t num_q_heads, int32_t num_kv_heads,
+                                                     int32_t head_dim, int32_t dtype) {
+  if (batch < 1 || total_nodes < 1 || max_nodes < 1 || max_prefix_len < 0 || num_q_heads < 1 ||
+      num_kv_heads < 1)
+    return 0;
+  return plan_attn(batch, total_nodes, max_nodes, max_prefix_len, num_q_heads, num_kv_heads,
+                   head_dim, dtype).workspace;
+}
+
+extern "C" tv_status_t tv_tree_verify_attn(
+    const void* q, const void* k_cache, const void* v_cache, int32_t num_pages,
+    const int32_t* block_table, int32_t max_pages_per_req, const int32_t* prefix_len,
+    const int32_t* cu_nodes, int32_t batch, int32_t total_nodes, int32_t max_nodes,
+    int32_t max_prefix_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t page_size, int32_t dtype, float softmax_scale, const tv_mask_t* mask, void* out,
+    float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !prefix_len || !cu_nodes || !mask || !out)
+    return TV_ERR_INVALID_ARGUMENT;
+  if (batch < 1 || total_nodes < 1 || max_nodes < 1 || max_prefix_len < 0 || num_pages < 1 ||
+      max_pages_per_req < 1 || num_q_heads < 1 || num_kv_heads < 1 || page_size < 1)
+    return TV_ERR_INVALID_ARGUMENT;
+  if (num_q_heads % num_kv_heads) return TV_ERR_INVALID_ARGUMENT;
+  if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_INVALID_ARGUMENT;
+  if (head_dim != 64 && head_dim != 128) return TV_ERR_UNSUPPORTED;
+  if (page_size % 4) return TV_ERR_UNSUPPORTED;
+  // 32-bit index arithmetic inside the kernels
+  if ((int64_t)num_pages * num_kv_heads * page_size >= (int64_t(1) << 31) ||
+      (int64_t)total_nodes * num_q_heads >= (int64_t(1) << 31) ||
+      (int64_t)batch * max_pages_per_req >= (int64_t(1) << 31))
+    return TV_ERR_UNSUPPORTED;
+  MaskDev md{mask->kind, mask->words_per_node, mask->bits, mask->anchor_pos, mask->branch_depth};
+  if (md.kind == TV_MASK_BITS) {
+    if (!md.bits || md.words < 1) return TV_ERR_INVALID_ARGUMENT;
+    if ((int64_t)md.words * 64 < max_nodes) return TV_ERR_INVALID_ARGUMENT;
+  } else if (md.kind == TV_MASK_ANCHOR) {
+    if (!md.anchor_pos || !md.branch_depth) return TV_ERR_INVALID_ARGUMENT;
+  } else {
+    return TV_ERR_INVALID_ARGUMENT;
+  }
+  const AttnPlan plan = plan_attn(batch, total_nodes, max_nodes, max_prefix_len, num_q_heads,
+                                  num_kv_heads, head_dim, dtype);
+  if ((int64_t)batch * num_kv_heads * plan.row_blocks * plan.splits >= (int64_t(1) << 31))
+    return TV_ERR_UNSUPPORTED;
+  if (plan.workspace > 0) {
+    if (!workspace || workspace_bytes < plan.workspace) return TV_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255) return TV_ERR_INVALID_ARGUMENT;
+  }
+  AttnArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_pages = num_pages;
+  a.block_table = block_table;
+  a.max_pages = max_pages_per_req;
+  a.prefix_len = prefix_len;
+  a.cu_nodes = cu_nodes;
+  a.batch = batch;
+  a.total_nodes = total_nodes;
+  a.max_nodes = max_nodes;
+  a.max_prefix_len = max_prefix_len;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.head_dim = head_dim;
+  a.page_size = page_size;
+  a.dtype = dtype;
+  a.scale = softmax_scale;
+  a.mask = md;
+  a.out = out;
+  a.lse = lse;
+  a.workspace = workspace;
+  return launched(launch_attn(a, plan, stream));
+}
+
+extern "C" tv_status_t tv_tree_accept(const int32_t* parent, const int32_t* draft_tok,
+                                      const int32_t* target_tok, const int32_t* cu_nodes,
+                                      int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                                      int32_t max_depth, int32_t* accept_len, int32_t* path,
+                                      int32_t* bonus_tok, hipStream_t stream) {
+  if (!parent || !draft_tok || !target_tok || !cu_nodes || !accept_len || !path)
+    return TV_ERR_INVALID_ARGUMENT;
+  if (batch < 1 || total_nodes < 0 || max_nodes < 1 || max_depth < 0) return TV_ERR_INVALID_ARGUMENT;
+  if (max_nodes > TV_MAX_ACCEPT_NODES) return TV_ERR_UNSUPPORTED;
+  return launched(launch_accept(parent, draft_tok, target_tok, cu_nodes, batch, total_nodes,
+                                max_nodes, max_depth, accept_len, path, bonus_tok, stream));
+}
