@@ -148,15 +148,21 @@ def _tree_tokens(rng, parent, vocab, match_p):
     draft[0] = int(rng.integers(vocab))
     for i in range(n):
         if ch[i]:
-            toks = _distinct(rng, len(ch[i]), vocab)
+            # distinct siblings when the vocabulary allows it (tiny test vocabularies
+            # with more children than tokens repeat tokens among siblings)
+            if len(ch[i]) <= vocab:
+                toks = _distinct(rng, len(ch[i]), vocab)
+            else:
+                toks = [int(t) for t in rng.integers(vocab, size=len(ch[i]))]
             for c, t in zip(ch[i], toks):
                 draft[c] = t
     target = np.zeros(n, np.int32)
     for i in range(n):
+        taken = {int(draft[c]) for c in ch[i]}
         if ch[i] and rng.random() < match_p[i]:
             target[i] = draft[ch[i][int(rng.integers(len(ch[i])))]]
-        elif ch[i]:
-            target[i] = _distinct(rng, 1, vocab, exclude=[int(draft[c]) for c in ch[i]])[0]
+        elif ch[i] and len(taken) < vocab:
+            target[i] = _distinct(rng, 1, vocab, exclude=taken)[0]
         else:
             target[i] = int(rng.integers(vocab))
     return draft, target
