@@ -143,21 +143,23 @@ size_t tv_tree_verify_attn_workspace_size(int32_t batch, int32_t total_nodes, in
  *   s_p    = softmax_scale * <q[i,h,:], K[p,g,:]>
  *   out    = sum_p softmax(s)_p V[p,g,:]        lse = ln sum_p exp(s_p)
  * where K/V at logical position p of request b live in page
- * block_table[b*max_pages_per_req + p/page_size], slot p % page_size.
+ * block_table[b*max_pages_per_req + p/page_size], slot p % page_size:
+ * K[p,g,:] = k_cache[page][g][slot][:], V[p,g,d] = v_cache[page][g][d][slot].
  * The tree nodes' own K/V are at positions P .. P+n-1 (written by the caller).
  *
  *   q            [total_nodes][num_q_heads][head_dim]            dtype
  *   k_cache      [num_pages][num_kv_heads][page_size][head_dim]  dtype
- *   v_cache      same layout as k_cache
+ *   v_cache      [num_pages][num_kv_heads][head_dim][page_size]  dtype (d-major pages:
+ *                the page_size keys of one (kv head, d) are contiguous)
  *   num_pages    (host) pages in the caches; page ids are clamped into range
  *   block_table  [batch][max_pages_per_req]  entries past a request's last page are not read
  *   prefix_len   [batch]
  *   cu_nodes     [batch + 1]
  *   max_prefix_len (host) >= every prefix_len
  *   head_dim     64 or 128;  num_q_heads % num_kv_heads == 0
- *   page_size    multiple of 4 (16 in the measured configurations)
+ *   page_size    a power of two >= 16 (16 in the measured configurations)
  *   dtype        TV_BF16 (MFMA path) or TV_F32 (fp32 VALU path)
- *   softmax_scale usually 1/sqrt(head_dim)
+ *   softmax_scale > 0 and finite, usually 1/sqrt(head_dim)
  *   mask         (host) struct of device pointers, typically from tv_tree_mask_build
  *                (ANCHOR needs every request in anchor form)
  *   out          [total_nodes][num_q_heads][head_dim]  dtype (round to nearest even)

@@ -107,7 +107,8 @@ def tree_attn(q, k_cache, v_cache, block_table, prefix_len, cu_nodes, parent,
               formulation: str = "dense"):
     """Attention of every (node, head) row -- or of the listed ``rows`` -- in fp64.
 
-    ``q`` is [N, Hq, D]; caches are [pages, Hkv, page_size, D]; ``rows`` is an
+    ``q`` is [N, Hq, D]; the K cache is [pages, Hkv, page_size, D] and the V
+    cache [pages, Hkv, D, page_size] (d-major pages); ``rows`` is an
     optional int array [R, 2] of (global node, q head).  Returns
     (out float64 [N, Hq, D] or [R, D], lse float64 [N, Hq] or [R]).
     """
@@ -124,7 +125,8 @@ def tree_attn(q, k_cache, v_cache, block_table, prefix_len, cu_nodes, parent,
     d = q.shape[-1]
     page = kc.shape[2]
     assert q.shape == (n, num_q_heads, d)
-    assert kc.shape[1] == num_kv_heads and kc.shape[3] == d and vc.shape == kc.shape
+    assert kc.shape[1] == num_kv_heads and kc.shape[3] == d
+    assert vc.shape == (kc.shape[0], num_kv_heads, d, page)
     assert bt.ndim == 2 and bt.shape[0] == batch
     if rows is None:
         out = np.zeros((n, num_q_heads, d), np.float64)

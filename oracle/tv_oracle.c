@@ -23,7 +23,8 @@
  *   - the K/V of local tree node j of request b sits at logical cache position
  *     prefix_len[b] + j, right after that request's prefix;
  *   - logical position p of request b lives in page block_table[b*max_pages + p/page_size],
- *     slot p % page_size; caches are laid out [page][kv_head][slot][head_dim];
+ *     slot p % page_size; the K cache is laid out [page][kv_head][slot][head_dim]
+ *     and the V cache [page][kv_head][head_dim][slot] (d-major pages);
  *   - query head h reads kv head h / (Hq / Hkv) (contiguous GQA groups);
  *   - q and out are [node][q_head][head_dim], lse is [node][q_head].
  */
@@ -135,7 +136,7 @@ void orc_mask_anchor(const int32_t* parent, const int32_t* cu_nodes, int32_t bat
 typedef struct {
   const float* q;          /* [N_tot][Hq][D] */
   const float* k_cache;    /* [num_pages][Hkv][page][D] */
-  const float* v_cache;
+  const float* v_cache;    /* [num_pages][Hkv][D][page] */
   const int32_t* block_table; /* [batch][max_pages] */
   const int32_t* prefix_len;  /* [batch] */
   const int32_t* cu_nodes;    /* [batch+1] */
@@ -144,11 +145,16 @@ typedef struct {
   double scale;
 } orc_attn_args;
 
-static const float* orc_kv_row(const orc_attn_args* a, const float* cache, int b,
-                               int pos, int g) {
+static const float* orc_k_row(const orc_attn_args* a, int b, int pos, int g) {
   int page = a->block_table[(size_t)b * a->max_pages + pos / a->page];
   int slot = pos % a->page;
-  return cache + (((size_t)page * a->hkv + g) * a->page + slot) * a->d;
+  return a->k_cache + (((size_t)page * a->hkv + g) * a->page + slot) * a->d;
+}
+
+static double orc_v_at(const orc_attn_args* a, int b, int pos, int g, int t) {
+  int page = a->block_table[(size_t)b * a->max_pages + pos / a->page];
+  int slot = pos % a->page;
+  return (double)a->v_cache[(((size_t)page * a->hkv + g) * a->d + t) * a->page + slot];
 }
 
 static double orc_dot(const float* x, const float* y, int d) {
@@ -176,7 +182,7 @@ static void orc_attn_row_dense(const orc_attn_args* a, int b, int i, int h,
   for (int p = 0; p < nk; ++p) {
     int visible = p < P || vis[p - P];
     if (!visible) { scores[p] = -INFINITY; continue; }
-    scores[p] = a->scale * orc_dot(qrow, orc_kv_row(a, a->k_cache, b, p, g), a->d);
+    scores[p] = a->scale * orc_dot(qrow, orc_k_row(a, b, p, g), a->d);
     if (scores[p] > m) m = scores[p];
   }
   double l = 0.0;
@@ -185,8 +191,7 @@ static void orc_attn_row_dense(const orc_attn_args* a, int b, int i, int h,
     if (scores[p] == -INFINITY) continue;
     double w = exp(scores[p] - m);
     l += w;
-    const float* vrow = orc_kv_row(a, a->v_cache, b, p, g);
-    for (int t = 0; t < a->d; ++t) out[t] += w * (double)vrow[t];
+    for (int t = 0; t < a->d; ++t) out[t] += w * orc_v_at(a, b, p, g, t);
   }
   for (int t = 0; t < a->d; ++t) out[t] /= l;
   *lse = m + log(l);
@@ -210,7 +215,7 @@ static void orc_attn_row_path(const orc_attn_args* a, int b, int i, int h,
   for (int j = i; j != -1; j = par[j]) keys[pos--] = P + j;
   double m = -INFINITY;
   for (int t = 0; t < nk; ++t) {
-    scores[t] = a->scale * orc_dot(qrow, orc_kv_row(a, a->k_cache, b, keys[t], g), a->d);
+    scores[t] = a->scale * orc_dot(qrow, orc_k_row(a, b, keys[t], g), a->d);
     if (scores[t] > m) m = scores[t];
   }
   double l = 0.0;
@@ -218,8 +223,7 @@ static void orc_attn_row_path(const orc_attn_args* a, int b, int i, int h,
   for (int t = 0; t < nk; ++t) {
     double w = exp(scores[t] - m);
     l += w;
-    const float* vrow = orc_kv_row(a, a->v_cache, b, keys[t], g);
-    for (int e = 0; e < a->d; ++e) out[e] += w * (double)vrow[e];
+    for (int e = 0; e < a->d; ++e) out[e] += w * orc_v_at(a, b, keys[t], g, e);
   }
   for (int e = 0; e < a->d; ++e) out[e] /= l;
   *lse = m + log(l);

@@ -40,7 +40,7 @@ def test_status_strings():
 def test_workspace_size_is_a_pure_host_query():
     lib = tv.load_library()
     ws = lib.tv_tree_verify_attn_workspace_size
-    assert ws(1, 60, 60, 64, 32, 8, 128, 1) == 0           # short prefix: one key split
+    assert ws(1, 60, 60, 4, 32, 8, 128, 1) == 0            # 64 keys fit one tile: one key split
     big = ws(1, 60, 60, 2048, 32, 8, 128, 1)
     assert big > 0 and big % 256 == 0
     assert ws(1, 60, 60, 2048, 32, 8, 128, 0) == 0         # fp32 path never splits
@@ -67,6 +67,7 @@ def test_attn_argument_checks():
     assert _attn(lib, dtype=7) == 1
     assert _attn(lib, d=96) == 2
     assert _attn(lib, page=6) == 2
+    assert _attn(lib, page=48) == 2          # not a power of two
     assert _attn(lib, batch=0) == 1
     assert _attn(lib, maxn=65) == 1          # one mask word cannot hold 65 nodes
     assert _attn(lib) == 3                   # a 2048-key prefix needs split workspace

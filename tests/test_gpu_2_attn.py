@@ -80,6 +80,17 @@ def test_head_layouts(hq, hkv, d):
     _run_and_check(w, "heads %d/%d d=%d" % (hq, hkv, d))
 
 
+@pytest.mark.parametrize("page,d,dtype", [(32, 128, "bf16"), (64, 64, "bf16"), (256, 128, "bf16"),
+                                           (32, 64, "f32")])
+def test_larger_pages(page, d, dtype):
+    """Pages of 32..256 keys: a 64-key tile spans one or several tiles per page."""
+    rng = np.random.default_rng(page + d)
+    trees = [list(W.GRAFT_TREE_PARENT), W.random_tree(rng, 90), W.random_tree(rng, 7)]
+    w = W.build_workload("pages", trees, [700, 31, 260], 8, 2, d, dtype, rng, page_size=page,
+                         permute_pages=True, spare_pages=3, tokens=False)
+    _run_and_check(w, "page=%d d=%d %s" % (page, d, dtype))
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_fp32_path(d):
     rng = np.random.default_rng(d)
@@ -105,7 +116,7 @@ def test_unused_cache_slots_are_never_read():
         end = int(w.prefix_len[b]) + int(w.nodes_per_request[b])
         last = w.block_table[b, (end - 1) // 16]
         kk[last, :, (end - 1) % 16 + 1:] = float("nan")
-        vv[last, :, (end - 1) % 16 + 1:] = float("nan")
+        vv[last, :, :, (end - 1) % 16 + 1:] = float("nan")
     w.k_cache, w.v_cache = kk, vv
     d = Dev(w)
     out, lse = d.attn()
@@ -121,7 +132,7 @@ def test_non_ancestor_kv_leaves_outputs_unchanged():
     pos = int(w.prefix_len[0]) + j
     page, slot = int(w.block_table[0, pos // 16]), pos % 16
     d.k[page, :, slot] += 3
-    d.v[page, :, slot] -= 2
+    d.v[page, :, :, slot] -= 2
     out, _ = d.attn()
     anc = np.zeros(60, bool)
     for i in range(60):

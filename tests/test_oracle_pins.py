@@ -145,7 +145,7 @@ def gathered_kv(w, b):
     pages = torch.from_numpy(w.block_table[b, pos // w.page_size].astype(np.int64))
     slots = torch.from_numpy(pos % w.page_size)
     k = w.k_cache.double()[pages, :, slots, :].permute(1, 0, 2)
-    v = w.v_cache.double()[pages, :, slots, :].permute(1, 0, 2)
+    v = w.v_cache.double()[pages, :, :, slots].permute(1, 0, 2)
     return k, v
 
 
@@ -202,7 +202,7 @@ def test_single_node_no_prefix_returns_its_own_value(oracle_lib):
                                 w.cu_nodes, w.parent, 8, 2, w.scale)
     for h in range(8):
         g = h // 4
-        np.testing.assert_array_equal(out[0, h], w.v_cache[0, g, 0].double().numpy())
+        np.testing.assert_array_equal(out[0, h], w.v_cache[0, g, :, 0].double().numpy())
         s = float((w.q[0, h].double() * w.k_cache[0, g, 0].double()).sum()) * w.scale
         assert abs(lse[0, h] - s) < 1e-12
 
@@ -251,7 +251,7 @@ def test_non_ancestor_kv_does_not_matter(oracle_lib):
     pos = P + j
     page, slot = w.block_table[0, pos // 16], pos % 16
     w.k_cache[page, :, slot] += 3.0
-    w.v_cache[page, :, slot] -= 2.0
+    w.v_cache[page, :, :, slot] -= 2.0
     out, _ = oracle.tree_attn(w.q, w.k_cache, w.v_cache, w.block_table, w.prefix_len,
                               w.cu_nodes, w.parent, 8, 2, w.scale)
     for i in range(len(tree)):

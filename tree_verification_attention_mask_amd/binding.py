@@ -145,13 +145,14 @@ def tree_verify_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
                      workspace: torch.Tensor | None = None, stream=None):
     """One tree-verification attention layer (``tv_tree_verify_attn``).
 
-    ``q`` [N, Hq, D]; caches [pages, Hkv, page, D] (bf16 or fp32);
+    ``q`` [N, Hq, D]; ``k_cache`` [pages, Hkv, page, D], ``v_cache`` [pages, Hkv, D, page]
+    (bf16 or fp32);
     ``block_table`` int32 [B, max_pages]; returns (out [N, Hq, D], lse [N, Hq] or None).
     """
     lib = load_library()
     n, hq, d = q.shape
     pages, hkv, page, d2 = k_cache.shape
-    assert d2 == d and v_cache.shape == k_cache.shape
+    assert d2 == d and tuple(v_cache.shape) == (pages, hkv, d, page)
     assert q.dtype == k_cache.dtype == v_cache.dtype and q.is_contiguous()
     assert k_cache.is_contiguous() and v_cache.is_contiguous() and block_table.is_contiguous()
     batch = cu_nodes.numel() - 1

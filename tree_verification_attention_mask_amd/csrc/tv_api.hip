@@ -69,8 +69,9 @@ extern "C" tv_status_t tv_tree_verify_attn(
     return TV_ERR_INVALID_ARGUMENT;
   if (num_q_heads % num_kv_heads) return TV_ERR_INVALID_ARGUMENT;
   if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_INVALID_ARGUMENT;
+  if (!(softmax_scale > 0.f) || !(softmax_scale < 3.0e38f)) return TV_ERR_INVALID_ARGUMENT;
   if (head_dim != 64 && head_dim != 128) return TV_ERR_UNSUPPORTED;
-  if (page_size % 4) return TV_ERR_UNSUPPORTED;
+  if (page_size < 16 || (page_size & (page_size - 1))) return TV_ERR_UNSUPPORTED;
   // 32-bit index arithmetic inside the kernels
   if ((int64_t)num_pages * num_kv_heads * page_size >= (int64_t(1) << 31) ||
       (int64_t)total_nodes * num_q_heads >= (int64_t(1) << 31) ||

@@ -92,7 +92,8 @@ struct AttnArgs {
 // Launch plan of the bf16 path: rows per block, key splits. A pure function
 // of host scalars, shared by the workspace query and the launch.
 struct AttnPlan {
-  int rw;              // 16-row subtiles per wave (block rows = 64 * rw)
+  int waves;           // wavefronts per workgroup (4 or 8)
+  int rw;              // 16-row subtiles per wave (block rows = 16 * waves * rw)
   int row_blocks;      // blocks over the node*group rows of one kv head
   int splits;          // key splits
   int keys_per_split;  // multiple of 64

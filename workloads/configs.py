@@ -72,7 +72,7 @@ class Workload:
     num_pages: int
     q: torch.Tensor                # [N_tot, Hq, D]
     k_cache: torch.Tensor          # [num_pages, Hkv, page, D]
-    v_cache: torch.Tensor
+    v_cache: torch.Tensor          # [num_pages, Hkv, D, page] (d-major pages)
     draft_tok: np.ndarray | None   # int32 [N_tot]
     target_tok: np.ndarray | None  # int32 [N_tot]
     max_depth: int                 # deepest node over the batch
@@ -190,7 +190,7 @@ def build_workload(name: str, trees: Sequence[Sequence[int]], prefix_len: Sequen
 
     ``match_p`` is a float or ``f(request, depths) -> per-node probability``.
     The K/V of request b's tree node j sits at logical position
-    prefix_len[b] + j.  Pages are handed out request by request (identity
+    prefix_len[b] + j. K pages are [Hkv, page, D], V pages [Hkv, D, page].  Pages are handed out request by request (identity
     table) or, with ``permute_pages``, through a seeded permutation of the
     whole pool.  ``spare_pages`` adds unused pages to the pool.
     """
@@ -231,7 +231,7 @@ def build_workload(name: str, trees: Sequence[Sequence[int]], prefix_len: Sequen
     n_tot = int(cu[-1])
     q = _normal(rng, (n_tot, num_q_heads, head_dim), tdt)
     k = _normal(rng, (num_pages, num_kv_heads, page_size, head_dim), tdt)
-    v = _normal(rng, (num_pages, num_kv_heads, page_size, head_dim), tdt)
+    v = _normal(rng, (num_pages, num_kv_heads, head_dim, page_size), tdt)
     return Workload(name=name, batch=batch, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                     head_dim=head_dim, page_size=page_size, dtype=dtype, parent=parent,
                     cu_nodes=cu, prefix_len=np.asarray(prefix_len, np.int32), block_table=table,
