@@ -36,6 +36,7 @@
 // (d-major V pages: 16 consecutive keys of one d are contiguous, which is the
 // V^T operand layout of the PV product).
 #include <algorithm>
+#include <type_traits>
 
 #include "tv_internal.h"
 
@@ -51,6 +52,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kTile = 64;     // keys per tile
 constexpr int kNumCUs = 256;  // MI355X compute units (the launch plan targets one pass over them)
 constexpr int kMaxSplitPages = 4096;  // page ids one workgroup can stage (16-token pages: 64K keys)
+constexpr float kLazyMax = 8.f;      // running-max slack before O is rescaled (log2 units)
 
 struct Params {
   const __bf16* q;
@@ -86,7 +88,7 @@ __device__ __forceinline__ uint32_t hi16x2(uint32_t a, uint32_t b) {  // {a.hi, 
 // equal and drops one of them.
 __device__ __forceinline__ void swap_pair(uint32_t u, bool rows32, uint32_t& a, uint32_t& b) {
   uint32_t w = u;
-  asm volatile("" : "+v"(w));
+  asm("" : "+v"(w));
   if (rows32) {
     const auto r = __builtin_amdgcn_permlane32_swap(u, w, false, false);
     a = r[0]; b = r[1];
@@ -116,6 +118,15 @@ __device__ __forceinline__ float row_sum4(float v) {
 // insertion does not model it -- it would put a vmcnt(0) before any LDS read
 // of the same array and drain the tile pipeline; the pipeline waits for
 // these loads itself (counted vmcnt, then a barrier). M0 is restored.
+// s_waitcnt operand that waits for nothing (gfx9 encoding: vmcnt bits 3:0
+// and 15:14, expcnt 6:4, lgkmcnt 11:8), and a wait for vmcnt <= N.
+constexpr int W_ALL = (15) | (3 << 14) | (7 << 4) | (15 << 8);
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((W_ALL & ~0xC00F) | (N & 15) | ((N >> 4) << 14));
+}
+
 __device__ __forceinline__ void lds_dma16(const void* src, const void* lds) {
   const uint32_t a = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
@@ -131,7 +142,7 @@ __device__ __forceinline__ void lds_dma16(const void* src, const void* lds) {
 }
 
 template <int D, int NW, int RW, bool WIDE>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 1 : 2)))
 void attn_bf16_kernel(Params p) {
   constexpr int T = 64 * NW;           // threads
   constexpr int DS = D / 32;           // 32-wide d steps of S^T = K Q^T
@@ -145,13 +156,15 @@ void attn_bf16_kernel(Params p) {
   constexpr int IPW = INS / NW;        // ... per wave
   constexpr int RPI = 512 / D;         // K rows per load (1 KB / row bytes)
   constexpr int VPG = D / 32;          // V loads per 16-key group (32 d rows each)
-  static_assert(INS % NW == 0, "load split");
+  constexpr int GPW = (NW == 8) ? 1 : 2;  // 16-key groups one wave loads per tile
+  constexpr int PPT = kMaxSplitPages / T;  // page-table entries per thread
+  static_assert(INS % NW == 0 && IPW * RPI == 16 * GPW && IPW == VPG * GPW, "load split");
   // Ring of STAGES tiles: K as [key][d] with 16-byte chunks XOR-swizzled by
   // key (conflict-free A-operand reads), V as [16-key group][d][16 keys] (the
   // V^T operand layout, copied as is from the d-major V pages).
   __shared__ __attribute__((aligned(16))) __bf16 sK[STAGES][TILE_E];
   __shared__ __attribute__((aligned(16))) __bf16 sV[STAGES][TILE_E];
-  __shared__ int s_pages[kMaxSplitPages];  // page ids of this block's key range
+  __shared__ int s_pages[kMaxSplitPages];  // page ids of this block's key window
   __shared__ int s_bounds[4];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -166,6 +179,24 @@ void attn_bf16_kernel(Params p) {
   wg /= p.row_blocks;
   const int g = wg % p.hkv;
   const int b = wg / p.hkv;
+  const int ks = split * p.keys_per_split;
+
+  // Page ids of the split's key window [ks, ks + keys_per_split + 64): their
+  // loads do not depend on the request's bounds, so both are in flight at
+  // once. Entries past the request's last page are never used for a key.
+  const int lp = __builtin_ctz(p.page_size);  // page_size == 1 << lp
+  const int pmask = p.page_size - 1;
+  const int pg_lo = ks >> lp;
+  const int n_pg = max(1, min(((ks + p.keys_per_split + kTile - 1) >> lp) - pg_lo + 1, kMaxSplitPages));
+  int pgv[PPT];
+  {
+    const int32_t* row_tab = p.block_table + (size_t)b * p.max_pages;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int i = tid + j * T;
+      pgv[j] = (i < n_pg) ? row_tab[min(pg_lo + i, p.max_pages - 1)] : 0;
+    }
+  }
 
   const int n0 = clampi(p.cu_nodes[b], 0, p.total_nodes);
   const int n = clampi(p.cu_nodes[b + 1], n0, p.total_nodes) - n0;
@@ -175,12 +206,16 @@ void attn_bf16_kernel(Params p) {
   const int row0 = rb * MBLK;
   if (row0 >= rows) return;
   const int kv_end = P + n;
-  const int ks = split * p.keys_per_split;
   if (ks >= kv_end) return;  // split absent for this request; the merge skips it
   // Ancestors-or-self have smaller indices, so no key past the block's last
   // node is visible to any of its rows.
   const int node_hi = min(n - 1, (row0 + MBLK - 1) / G);
   const int ke = min(min(ks + p.keys_per_split, kv_end), P + node_hi + 1);
+#pragma unroll
+  for (int j = 0; j < PPT; ++j) {
+    const int i = tid + j * T;
+    if (i < n_pg) s_pages[i] = clampi(pgv[j], 0, p.num_pages - 1);
+  }
 
   // ANCHOR form: block-wide bounds to skip tree tiles no row can see and to
   // treat tiles every row sees in full as unmasked.
@@ -221,7 +256,8 @@ void attn_bf16_kernel(Params p) {
   // subtile, d = 32s + 8q4 .. +7. Subtiles st = wave + NW r hold rows
   // row0 + 16 st ..; the first nv of them (a wave-uniform count) have a real
   // row. Padding rows carry zero Q and are never stored, so the MFMAs below
-  // run unguarded.
+  // run unguarded. These loads, and the mask rows', stay in flight while the
+  // first K/V tiles are requested.
   int nv = 0;
 #pragma unroll
   for (int r = 0; r < RW; ++r) nv += (row0 + 16 * (wave + NW * r) < rows) ? 1 : 0;
@@ -242,28 +278,24 @@ void attn_bf16_kernel(Params p) {
     rloc[r] = i;
     rnode[r] = n0 + i;
     orow[r] = (n0 + i) * p.hq + g * G + hl;
+    // unconditional loads (a padding row reads the request's first row and
+    // drops it): a per-lane branch here would wait for each load in turn
+    m_w0[r] = 0ull; m_w1[r] = 0ull;
+    if (anchor) {
+      const uint64_t a = (uint64_t)(uint32_t)p.mask.anchor_pos[rnode[r]] |
+                         ((uint64_t)(uint32_t)p.mask.branch_depth[rnode[r]] << 32);
+      m_w0[r] = row_ok[r] ? a : 0ull;
+    } else if (bits_in_regs) {
+      const uint64_t w0 = p.mask.bits[(size_t)rnode[r] * p.mask.words];
+      const uint64_t w1 = p.mask.bits[(size_t)rnode[r] * p.mask.words + (p.mask.words - 1)];
+      m_w0[r] = row_ok[r] ? w0 : 0ull;
+      m_w1[r] = (row_ok[r] && p.mask.words == 2) ? w1 : 0ull;
+    }
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      if (row_ok[r]) {
-        const uint4 u = *reinterpret_cast<const uint4*>(p.q + (size_t)orow[r] * D + 32 * s + 8 * q4);
-        qf[r][s] = __builtin_bit_cast(bf16x8, u);
-      } else {
-        qf[r][s] = bf16x8{};
-      }
+      const uint4 u = *reinterpret_cast<const uint4*>(p.q + (size_t)orow[r] * D + 32 * s + 8 * q4);
+      qf[r][s] = row_ok[r] ? __builtin_bit_cast(bf16x8, u) : bf16x8{};
     }
-    m_w0[r] = 0ull; m_w1[r] = 0ull;
-    if (row_ok[r]) {
-      if (anchor) {
-        m_w0[r] = (uint64_t)(uint32_t)p.mask.anchor_pos[rnode[r]] |
-                  ((uint64_t)(uint32_t)p.mask.branch_depth[rnode[r]] << 32);
-      } else if (bits_in_regs) {
-        m_w0[r] = p.mask.bits[(size_t)rnode[r] * p.mask.words];
-        if (p.mask.words == 2) m_w1[r] = p.mask.bits[(size_t)rnode[r] * 2 + 1];
-      }
-    }
-    // keep these in registers: re-reading them inside the tile loop would
-    // make its masked tiles wait for every load in flight, prefetch included
-    asm volatile("" : "+v"(m_w0[r]), "+v"(m_w1[r]));
   }
   // Visibility of keys [k0, k0 + 64) for this lane's row of subtile r.
   auto row_visibility = [&](int r, int k0) -> uint64_t {
@@ -293,54 +325,44 @@ void attn_bf16_kernel(Params p) {
   };
 
   f32x4 o[RW][DU];
-  float m_run[RW], l_run[RW];
+  float m_run[RW], l_run[RW], alpha[RW];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     m_run[r] = -INFINITY;
     l_run[r] = 0.f;
+    alpha[r] = 1.f;
 #pragma unroll
     for (int u = 0; u < DU; ++u) o[r][u] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  bool rescale = false;  // some row of the wave raised its running max: O *= alpha
 
   // ---- direct-to-LDS staging (lds_dma16). Load m of wave w is number
   // ins = w*IPW + m of the tile: ins < K_INS copies K rows [ins*RPI, +RPI)
   // (lane l: row ins*RPI + l/CPR, whose LDS chunk l%CPR receives K chunk
   // (l%CPR) ^ (row%CPR)); otherwise V 16-key group j = (ins-K_INS)/VPG,
-  // d rows 32*((ins-K_INS)%VPG) + l/2, keys 8*(l%2) .. +7. The keys of one
-  // load share a 16-key group and pages hold a power of two >= 16 keys, so a
-  // load never crosses a page: its page id and slot are wave-uniform and
-  // only a per-lane constant element offset differs between lanes.
-  const int lp = __builtin_ctz(p.page_size);  // page_size == 1 << lp
-  const int pmask = p.page_size - 1;
-  long lane_off[IPW];
-  int tile_off[IPW];
+  // d rows 32*((ins-K_INS)%VPG) + l/2, keys 8*(l%2) .. +7. The first NW/2
+  // waves load K, the others V; either way the loads of one wave cover
+  // GPW whole 16-key groups, gw .. gw+GPW-1, and pages hold a power of two
+  // >= 16 keys, so each group lies in one page: one page id per group and
+  // tile, looked up a step ahead, and a per-lane constant offset.
+  const bool k_wave = wave < NW / 2;
+  const int gw = (k_wave ? wave : wave - NW / 2) * GPW;
+  int lane_off[IPW];
   int lds_off[IPW];  // element offset of the load inside one stage of sK / sV
 #pragma unroll
   for (int m = 0; m < IPW; ++m) {
     const int ins = wave * IPW + m;
-    if (ins < K_INS) {
+    if (k_wave) {
       const int row = ins * RPI + lane / CPR;
-      tile_off[m] = ins * RPI;
-      lane_off[m] = (long)(lane / CPR) * D + 8 * ((lane % CPR) ^ (row % CPR));
+      lane_off[m] = (lane / CPR) * D + 8 * ((lane % CPR) ^ (row % CPR));
       lds_off[m] = ins * RPI * D;
     } else {
       const int vi = ins - K_INS, jj = vi / VPG, dp = vi % VPG;
-      tile_off[m] = 16 * jj;
-      lane_off[m] = ((long)(32 * dp + lane / 2) << lp) + 8 * (lane % 2);
+      lane_off[m] = ((32 * dp + lane / 2) << lp) + 8 * (lane % 2);
       lds_off[m] = jj * 16 * D + 32 * dp * 16;
     }
   }
   const int last = kv_end - 1;
-  // Page ids of every key an issued tile can touch, [pg_lo, pg_hi], read
-  // once into LDS (clamped into the pool) and looked up from there.
-  const int pg_lo = ks >> lp;
-  const int pg_hi = min((min(ke + kTile, kv_end) - 1) >> lp, p.max_pages - 1);
-  const int n_pg = min(max(pg_hi - pg_lo + 1, 1), kMaxSplitPages);
-  {
-    const int32_t* row_tab = p.block_table + (size_t)b * p.max_pages;
-    for (int i = tid; i < n_pg; i += T)
-      s_pages[i] = clampi(row_tab[min(pg_lo + i, p.max_pages - 1)], 0, p.num_pages - 1);
-  }
   // page id (wave-uniform) of tile position pos; positions past the
   // request's last key use the last key's page: tiles past the end read
   // valid memory that the softmax masks out or whose V is zeroed
@@ -348,32 +370,47 @@ void attn_bf16_kernel(Params p) {
     const int i = min(max((min(pos, last) >> lp) - pg_lo, 0), n_pg - 1);
     return __builtin_amdgcn_readfirstlane(s_pages[i]);
   };
-  auto issue = [&](int stage, int k0) {
+  auto pages_for = [&](int k0, int (&pg)[GPW]) {
 #pragma unroll
-    for (int m = 0; m < IPW; ++m) {
-      const int ins = wave * IPW + m;
-      const int pos0 = k0 + tile_off[m];
-      const long blk = (long)(page_of(pos0) * p.hkv + g);
-      const int slot0 = pos0 & pmask;
-      if (ins < K_INS)
+    for (int l = 0; l < GPW; ++l) pg[l] = page_of(k0 + 16 * (gw + l));
+  };
+  auto issue = [&](int stage, int k0, const int (&pg)[GPW]) {
+    if (k_wave) {
+#pragma unroll
+      for (int m = 0; m < IPW; ++m) {
+        const int l = (m * RPI) / 16;
+        const int slot0 = (k0 + 16 * (gw + l) + (m * RPI) % 16) & pmask;
+        const long blk = (long)pg[l] * p.hkv + g;
         lds_dma16(p.k + (((blk << lp) + slot0) * D + lane_off[m]), &sK[stage][lds_off[m]]);
-      else
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < IPW; ++m) {
+        const int l = m / VPG;
+        const int slot0 = (k0 + 16 * (gw + l)) & pmask;
+        const long blk = (long)pg[l] * p.hkv + g;
         lds_dma16(p.v + (((blk * D) << lp) + slot0 + lane_off[m]), &sV[stage][lds_off[m]]);
+      }
     }
   };
 
-  // ---- S^T = K Q^T of the tile in stage `buf`
+  // ---- S^T = K Q^T of the tile in stage `buf`. Row 4c + i of subtile t of
+  // S^T (the A-operand row fed from LDS) is key key_of(t, 4c + i) =
+  // 32(t/2) + 8c + 4(t%2) + i, so the lane of query row r16 and column group
+  // c = q4 ends up with keys 32kk + 8q4 .. +7 of each 32-key half kk: eight
+  // consecutive keys, which is what its B operand of the PV product needs
+  // and what one 16-byte LDS read of V supplies.
+  auto key_of = [](int t, int m) { return 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3); };
   auto qk = [&](int buf, f32x4 (&sacc)[RW][4]) {
 #pragma unroll
     for (int r = 0; r < RW; ++r)
 #pragma unroll
       for (int t = 0; t < 4; ++t) sacc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (nv == 0) return;
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int krow = 16 * t + r16;
+        const int krow = key_of(t, r16);
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
             &sK[buf][krow * D + 8 * ((4 * s + q4) ^ (krow % CPR))]);
 #pragma unroll
@@ -382,38 +419,46 @@ void attn_bf16_kernel(Params p) {
       }
     }
   };
-
-  // ---- online softmax of tile k0 from its scores, then O^T += V^T P^T
-  auto softmax_pv = [&](int buf, int k0, f32x4 (&sacc)[RW][4]) {
-    if (nv == 0) return;
-    const bool masked = !full_tile(k0);
-    bf16x8 pf[RW][2];
+  // ---- scores of keys a row may not see -> -inf
+  auto apply_mask = [&](int k0, f32x4 (&sacc)[RW][4]) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      // this lane's 16 keys key_of(t, 4q4 + i) as bits 4t + i of `own`
+      const uint64_t sh = row_visibility(r, k0) >> (8 * q4);
+      const uint32_t own = (uint32_t)(sh & 0xffu) | ((uint32_t)(sh >> 32) & 0xffu) << 8;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sacc[r][t][i] = ((own >> (4 * t + i)) & 1u) ? sacc[r][t][i] : -INFINITY;
+    }
+  };
+  // ---- running max from a tile's (masked) scores. The max is raised only
+  // when it grows by more than kLazyMax (log2 units), so rows rarely need
+  // their O rescaled; probabilities stay <= 2^kLazyMax, exact in fp32 and
+  // rounded to bf16 with the same relative error as any other value.
+  auto row_update = [&](f32x4 (&sacc)[RW][4]) {
+    bool need = false;
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
       float mx = -INFINITY;
-      if (masked) {
-        // this lane's 16 keys 16t + 4q4 + i as bits 4t + i of `own`
-        const uint64_t sh = row_visibility(r, k0) >> (4 * q4);
-        const uint32_t own = (uint32_t)(sh & 0xfu) | (uint32_t)((sh >> 12) & 0xf0u) |
-                             (uint32_t)((sh >> 24) & 0xf00u) | (uint32_t)((sh >> 36) & 0xf000u);
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = ((own >> (4 * t + i)) & 1u) ? sacc[r][t][i] : -INFINITY;
-            sacc[r][t][i] = x;
-            mx = fmaxf(mx, x);
-          }
-      } else {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[r][t][i]);
-      }
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[r][t][i]);
       mx = row_max4(mx) * p.scale_log2;
-      const float m_new = fmaxf(m_run[r], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[r] - m_use);
+      const bool up = mx > m_run[r] + kLazyMax;
+      alpha[r] = up ? __builtin_amdgcn_exp2f(m_run[r] - mx) : 1.f;
+      need = need || (up && m_run[r] != -INFINITY);
+      m_run[r] = up ? mx : m_run[r];
+    }
+    rescale = __any(need);
+  };
+  // ---- probabilities of a tile (bf16 B operand of the PV product), l update
+  auto probs = [&](f32x4 (&sacc)[RW][4], bf16x8 (&pf)[RW][2]) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const float m_use = (m_run[r] == -INFINITY) ? 0.f : m_run[r];
       float part[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -425,16 +470,7 @@ void attn_bf16_kernel(Params p) {
           part[t] += e;
         }
       }
-      const float sum = row_sum4((part[0] + part[1]) + (part[2] + part[3]));
-      l_run[r] = l_run[r] * alpha + sum;
-      // o is zero while m_run is -inf, and alpha == 1 when the max held:
-      // rescale only if some row of the wave raised a finite running max
-      const bool moved = m_run[r] != -INFINITY && m_new > m_run[r];
-      m_run[r] = m_new;
-      if (__any(moved)) {
-#pragma unroll
-        for (int u = 0; u < DU; ++u) o[r][u] *= alpha;
-      }
+      l_run[r] = l_run[r] * alpha[r] + row_sum4((part[0] + part[1]) + (part[2] + part[3]));
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         bf16x8 f;
@@ -446,17 +482,16 @@ void attn_bf16_kernel(Params p) {
         pf[r][kk] = f;
       }
     }
-    // logical k of lane group q4, element e: keys 32kk + 4q4 + e (e < 4)
-    // and 32kk + 16 + 4q4 + (e - 4) (e >= 4)
+  };
+  // ---- O^T += V^T P^T of the tile in stage `buf`. Element e of lane group
+  // q4 is key 32kk + 8q4 + e: 16-key group 2kk + q4/2, keys 8(q4%2) .. +7.
+  auto pv = [&](int buf, const bf16x8 (&pf)[RW][2]) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int u = 0; u < DU; ++u) {
-        // keys 32kk + 4q4 + e live in group 2kk, keys 32kk + 16 + .. in 2kk + 1
-        const __bf16* vg = &sV[buf][(2 * kk) * 16 * D + (16 * u + r16) * 16 + 4 * q4];
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vg);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vg + 16 * D);
-        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
+            &sV[buf][(2 * kk + (q4 >> 1)) * 16 * D + (16 * u + r16) * 16 + 8 * (q4 & 1)]);
 #pragma unroll
         for (int r = 0; r < RW; ++r)
           o[r][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[r][kk], o[r][u], 0, 0, 0);
@@ -464,17 +499,21 @@ void attn_bf16_kernel(Params p) {
     }
   };
 
-  // ---- pipeline. Tiles c0, c1, ... of the block; a step finishes tile c0
-  // (softmax + PV, its scores already in registers) while the scores of c1
-  // are computed -- independent MFMA work the scheduler interleaves with the
-  // softmax -- and c2, c3 are in flight. Each wave waits (counted vmcnt) for
-  // its own loads of c1 only, then a barrier makes every wave's loads
-  // visible; the same barrier proves every wave is done with the stage the
-  // step's new loads overwrite (tile c0 - 1's).
-  constexpr int W_ALL = (15) | (3 << 14) | (7 << 4) | (15 << 8);  // s_waitcnt: no-op base
-  auto wait_vm = [&](bool one_ahead) {  // wait until <= IPW (or 0) loads of this wave pend
-    if (one_ahead) __builtin_amdgcn_s_waitcnt((W_ALL & ~0xC00F) | (IPW & 15) | ((IPW >> 4) << 14));
-    else __builtin_amdgcn_s_waitcnt(W_ALL & ~0xC00F);
+  // ---- pipeline ("ping-pong"). Tiles c(0), c(1), ... of the block; per
+  // tile m two slots separated by barriers. The waves of group A
+  // (0 .. NW/2-1) run the MFMA cluster M(m) = [O += V(m-1)^T P(m-1)^T,
+  // S(m) = K(m) Q^T] in slot 2m and the VALU cluster V(m) = [mask, running
+  // max, rescale, P(m) = exp2(...)] in slot 2m+1; group B (NW = 8 only) runs
+  // the same clusters one slot later, so the two waves sharing a SIMD
+  // (w, w + 4) keep its matrix and vector pipes busy at the same time.
+  // Tile m+2 is requested at the start of slot 2m into the stage that tile
+  // m-2 left (its last reader, B's M(m-1), ended before that barrier); tile m
+  // must have landed by slot 2m: each wave waits (counted vmcnt) for its own
+  // loads of tile m, then the barrier makes every wave's loads visible.
+  // wait until at most `pending` loads of this wave are in flight
+  auto wait_vm = [&](int pending) {
+    if (pending >= IPW) wait_vmem<IPW>();
+    else wait_vmem<0>();
   };
   auto barrier = [&]() {
     asm volatile("" ::: "memory");
@@ -483,49 +522,121 @@ void attn_bf16_kernel(Params p) {
   };
   // zero the V columns of positions past the request's last key in a tile
   // that just landed (their K columns are masked; V must hold finite zeros
-  // for P = 0 to contribute nothing)
+  // for P = 0 to contribute nothing); the next barrier publishes them
   auto zero_tail = [&](int stage, int k0) {
-    if (k0 >= ke || k0 + kTile <= kv_end) return;
+    if (k0 + kTile <= kv_end) return;
     for (int e = tid; e < TILE_E; e += T) {
       const int key = 16 * (e / (16 * D)) + (e & 15);  // element (group, d, key%16)
       if (k0 + key >= kv_end) sV[stage][e] = static_cast<__bf16>(0.f);
     }
     __builtin_amdgcn_s_waitcnt(W_ALL & ~0x0F00);  // lgkmcnt(0): zeros written
-    barrier();
   };
-  int c0 = ks;
-  while (c0 < ke && skip_tile(c0)) c0 += kTile;
-  int c1 = next_tile(c0), c2 = next_tile(c1), c3 = next_tile(c2);
-  // the page list (and Q, mask rows) land here; then it is visible to all
-  __builtin_amdgcn_s_waitcnt(0);
+  const bool grp_b = (NW == 8) && wave >= NW / 2;
+  f32x4 sc[RW][4];
+  bf16x8 pf[RW][2];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) pf[r][0] = pf[r][1] = bf16x8{};
+  // M(m) runs both products unconditionally (no branches, so no copies of
+  // the accumulators at merge points): before the first tile P is zero and
+  // the V stage it reads was zeroed; after the last, the scores are unused.
+  auto cluster_m = [&](int m) {
+    if (nv == 0) return;
+    pv((m - 1) & (STAGES - 1), pf);
+    qk(m & (STAGES - 1), sc);
+    // software pipeline of the cluster: LDS fragment reads run kAhead
+    // fragments ahead of the MFMAs that consume them (RW MFMAs each), which
+    // hides LDS latency without holding every fragment in registers
+    constexpr int NFRAG = 2 * DU + 4 * DS;
+    constexpr int kAhead = 4;
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+    for (int f = 0; f < NFRAG - kAhead; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, RW, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, RW * kAhead, 0);
+  };
+  auto cluster_v = [&](int k0) {
+    if (nv == 0) return;
+    if (!full_tile(k0)) apply_mask(k0, sc);
+    row_update(sc);
+    if (rescale) {
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int u = 0; u < DU; ++u) o[r][u] *= alpha[r];
+    }
+    probs(sc, pf);
+  };
+
+  int c_cur = ks;
+  while (c_cur < ke && skip_tile(c_cur)) c_cur += kTile;
+  int c_prev = ke;  // tile m-1 (none yet)
+  int c_n1 = next_tile(c_cur), c_n2 = next_tile(c_n1);
+  // V of stage STAGES-1 is read (times P = 0) by the first M cluster
+  for (int e = tid; e < TILE_E; e += T) sV[STAGES - 1][e] = static_cast<__bf16>(0.f);
+  // the page list and the zeros are written; make them visible (Q and mask
+  // loads stay in flight)
+  __builtin_amdgcn_s_waitcnt(W_ALL & ~0x0F00);
   barrier();
-  if (c0 < ke) issue(0, c0);
-  if (c1 < ke) issue(1, c1);
-  if (c2 < ke) issue(2, c2);
-  f32x4 sA[RW][4], sB[RW][4];
-  int it = 0;
-  if (c0 < ke) {
-    if (c1 >= ke) wait_vm(false);
-    else if (c2 >= ke) wait_vm(true);
-    else __builtin_amdgcn_s_waitcnt((W_ALL & ~0xC00F) | ((2 * IPW) & 15) | (((2 * IPW) >> 4) << 14));
-    barrier();
-    zero_tail(0, c0);
-    qk(0, sA);
+  int pgn[GPW];
+  if (c_cur < ke) { pages_for(c_cur, pgn); issue(0, c_cur, pgn); }
+  if (c_n1 < ke) { pages_for(c_n1, pgn); issue(1, c_n1, pgn); }
+  pages_for(c_n2, pgn);
+  // Q fragments and mask rows are used from registers from here on (this
+  // waits for them, and for the two tiles just requested)
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    asm volatile("" : "+v"(m_w0[r]), "+v"(m_w1[r]));
+#pragma unroll
+    for (int s = 0; s < DS; ++s) asm volatile("" : "+v"(qf[r][s]));
   }
-  auto step = [&](f32x4 (&scur)[RW][4], f32x4 (&snext)[RW][4]) {
-    wait_vm(c2 < ke);  // tile c1 has landed (c2 may still be in flight)
+  int m = 0;
+  // start of slot 2m: tile m has landed and is visible, tile m+2 requested
+  auto head = [&]() {
+    if (c_cur < ke) wait_vm(c_n1 < ke ? IPW : 0);
     barrier();
-    zero_tail((it + 1) & (STAGES - 1), c1);
-    if (c3 < ke) issue((it + 3) & (STAGES - 1), c3);
-    if (c1 < ke) qk((it + 1) & (STAGES - 1), snext);
-    softmax_pv(it & (STAGES - 1), c0, scur);
-    c0 = c1; c1 = c2; c2 = c3; c3 = next_tile(c3);
-    ++it;
+    if (c_cur < ke) zero_tail(m & (STAGES - 1), c_cur);
+    if (c_n2 < ke) issue((m + 2) & (STAGES - 1), c_n2, pgn);
   };
-  while (c0 < ke) {
-    step(sA, sB);
-    if (c0 >= ke) break;
-    step(sB, sA);
+  auto advance = [&]() {
+    const int c_n3 = next_tile(c_n2);
+    pages_for(c_n3, pgn);
+    c_prev = c_cur; c_cur = c_n1; c_n1 = c_n2; c_n2 = c_n3;
+    ++m;
+  };
+  // Each group runs a straight loop (no per-slot branch between the two
+  // clusters, which would force copies of the accumulators); both execute
+  // 2 barriers per tile plus 2 at the end.
+  if (!grp_b) {
+    while (c_cur < ke) {
+      head();
+      cluster_m(m);
+      barrier();
+      cluster_v(c_cur);
+      advance();
+    }
+    head();
+    cluster_m(m);  // PV of the last tile
+    barrier();
+  } else {
+    if (c_cur < ke) {
+      head();
+      barrier();
+      cluster_m(m);
+      advance();
+    }
+    while (c_cur < ke) {
+      head();
+      cluster_v(c_prev);
+      barrier();
+      cluster_m(m);
+      advance();
+    }
+    head();
+    if (c_prev < ke) cluster_v(c_prev);
+    barrier();
+    cluster_m(m);  // PV of the last tile
   }
 
   // ---- epilogue: lane (r16, q4) holds O[row r16][16u + 4q4 + i]
@@ -750,15 +861,15 @@ AttnPlan plan_attn(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_
     pl.workspace = 0;
     return pl;
   }
-  // rows of one kv head: <= 64 -> 4 waves x 1 subtile (64 rows per block),
-  // <= 128 -> 8 waves x 1 (128 rows), else 8 waves x 2 (256 rows)
-  if (rows <= 64) { pl.waves = 4; pl.rw = 1; }
-  else if (rows <= 128) { pl.waves = 8; pl.rw = 1; }
-  else { pl.waves = 8; pl.rw = 2; }
-  const long mblk = 16L * pl.waves * pl.rw;
-  pl.row_blocks = (int)((rows + mblk - 1) / mblk);
+  // 8 waves (two groups sharing the SIMDs) x 1 subtile (128 rows per block);
+  // 8 x 2 (256 rows) when a kv head has more rows and keys enough for the
+  // larger block to amortise its longer per-tile step
   const long kv = (long)max_prefix_len + max_nodes;
   const long tiles = (kv + kTile - 1) / kTile;
+  pl.waves = 8;
+  pl.rw = (rows > 128 && tiles >= 48) ? 2 : 1;
+  const long mblk = 16L * pl.waves * pl.rw;
+  pl.row_blocks = (int)((rows + mblk - 1) / mblk);
   const long base = (long)batch * hkv * pl.row_blocks;
   // One 128 KB-LDS workgroup fits a CU: cut the keys into splits until the
   // workgroups cover the CUs once; more splits only add partial traffic.
