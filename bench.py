@@ -32,8 +32,43 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 VALU_FP32_PEAK_TFLOPS = 157.3
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ("tv_attn.hip", "tv_internal.h")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    """sha256 over the attention kernel's sources (ties counter data to a build)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "tree_verification_attention_mask_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per tree_verify_attn call from the committed counter summary
+    (rocprofv3 FETCH_SIZE / WRITE_SIZE passes scaled by a copy of known size),
+    or None when there is none or the kernel sources changed since."""
+    path = os.path.join(PROFILES, "tree_verify_attn_%s_hbm_counters.md" % workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel source sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["hbm bytes per call"])
+    except (KeyError, ValueError):
+        return None
 
 
 def depths(parent, cu):
@@ -100,6 +135,10 @@ def main():
     ap.add_argument("--rot", type=int, default=0, help="rotating buffer sets (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="before timing, copy this many MiB device to device three times "
+                         "(a plain copy of known size that hardware-counter passes use to "
+                         "scale FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
@@ -166,6 +205,16 @@ def main():
         mk = mask_call()
         attn_call(s, mk)
         accept_call()
+
+    if args.copy_probe_mb > 0:
+        src = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy probe: 3 x %d MiB device-to-device" % args.copy_probe_mb)
 
     for i in range(args.warmup):
         step(i % R)
@@ -247,7 +296,9 @@ def main():
                    "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
                    "mask": w.mask_kind, "rotating_buffer_sets": R, "hip_graph": True},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(w.name),
+                     "kernel_source_sha256": kernel_source_hash(),
                      "kernel": "tree_verify_attn (attn_bf16_kernel%s)" %
                                (" + combine_kernel" if plan_splits else ""),
                      "algorithmic_bytes_per_launch": alg_bytes,
