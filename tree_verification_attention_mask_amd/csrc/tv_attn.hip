@@ -72,14 +72,7 @@ struct Params {
   float scale_log2;  // softmax scale * log2(e), > 0
 };
 
-__device__ __forceinline__ uint32_t lo16x2(uint32_t a, uint32_t b) {  // {a.lo, b.lo}
-  return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t hi16x2(uint32_t a, uint32_t b) {  // {a.hi, b.hi}
-  return (a >> 16) | (b & 0xffff0000u);
-}
-
-// Max / sum over lanes l, l^16, l^32, l^48 (the 4 lanes holding one row of a
+// Sum / max over lanes l, l^16, l^32, l^48 (the 4 lanes holding one row of a
 // 16x16 accumulator). Every one of the 4 lanes gets bit-identical results.
 // v_permlane32_swap(x, y) leaves {x.lo | y.lo, x.hi | y.hi} in the two
 // registers, so with y a copy of x the pair holds x_l and x_(l^32) in every
@@ -97,19 +90,19 @@ __device__ __forceinline__ void swap_pair(uint32_t u, bool rows32, uint32_t& a, 
     a = r[0]; b = r[1];
   }
 }
-__device__ __forceinline__ float row_max4(float v) {
-  uint32_t a, b;
-  swap_pair(__builtin_bit_cast(uint32_t, v), true, a, b);
-  v = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
-  swap_pair(__builtin_bit_cast(uint32_t, v), false, a, b);
-  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
-}
 __device__ __forceinline__ float row_sum4(float v) {
   uint32_t a, b;
   swap_pair(__builtin_bit_cast(uint32_t, v), true, a, b);
   v = __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
   swap_pair(__builtin_bit_cast(uint32_t, v), false, a, b);
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float row_max4(float v) {
+  uint32_t a, b;
+  swap_pair(__builtin_bit_cast(uint32_t, v), true, a, b);
+  v = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  swap_pair(__builtin_bit_cast(uint32_t, v), false, a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 
 // Direct-to-LDS 16-byte load of every lane (global_load_lds_dwordx4): lane
@@ -171,14 +164,16 @@ void attn_bf16_kernel(Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int r16 = lane & 15, q4 = lane >> 4;
 
+  // block order: split fastest, then kv head, then request, row block
+  // slowest and last first -- later row blocks see more tree keys (causal
+  // trunks), so the longest workgroups of every head start first
   int wg = blockIdx.x;
   const int split = wg % p.splits;
   wg /= p.splits;
-  // later row blocks see more tree keys (causal trunks): dispatch them first
-  const int rb = p.row_blocks - 1 - wg % p.row_blocks;
-  wg /= p.row_blocks;
   const int g = wg % p.hkv;
-  const int b = wg / p.hkv;
+  wg /= p.hkv;
+  const int b = wg % p.batch;
+  const int rb = p.row_blocks - 1 - wg / p.batch;
   const int ks = split * p.keys_per_split;
 
   // Page ids of the split's key window [ks, ks + keys_per_split + 64): their
@@ -206,7 +201,20 @@ void attn_bf16_kernel(Params p) {
   const int row0 = rb * MBLK;
   if (row0 >= rows) return;
   const int kv_end = P + n;
-  if (ks >= kv_end) return;  // split absent for this request; the merge skips it
+  if (ks >= kv_end) {
+    // split absent for this request: mark its rows empty (m = -inf, l = 0)
+    // so that the merge needs no per-request bounds
+    if (p.splits > 1) {
+      const size_t R_tot = (size_t)p.total_nodes * p.hq;
+      for (int i = tid; i < min(MBLK, rows - row0); i += T) {
+        const int row = row0 + i;
+        const size_t orow_i = (size_t)(n0 + row / G) * p.hq + g * G + row % G;
+        *reinterpret_cast<float2*>(p.part_ml + ((size_t)split * R_tot + orow_i) * 2) =
+            float2{-INFINITY, 0.f};
+      }
+    }
+    return;
+  }
   // Ancestors-or-self have smaller indices, so no key past the block's last
   // node is visible to any of its rows.
   const int node_hi = min(n - 1, (row0 + MBLK - 1) / G);
@@ -325,11 +333,14 @@ void attn_bf16_kernel(Params p) {
   };
 
   f32x4 o[RW][DU];
-  float m_run[RW], l_run[RW], alpha[RW];
+  // fp32 row sums of P: each lane sums its own 16 keys of a row per tile;
+  // the 4 lanes of a row are added once, after the last tile
+  float l_lane[RW];
+  float m_run[RW], alpha[RW];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     m_run[r] = -INFINITY;
-    l_run[r] = 0.f;
+    l_lane[r] = 0.f;
     alpha[r] = 1.f;
 #pragma unroll
     for (int u = 0; u < DU; ++u) o[r][u] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -373,6 +384,20 @@ void attn_bf16_kernel(Params p) {
   auto pages_for = [&](int k0, int (&pg)[GPW]) {
 #pragma unroll
     for (int l = 0; l < GPW; ++l) pg[l] = page_of(k0 + 16 * (gw + l));
+  };
+  // the same lookup in two halves: the LDS read early, the result taken a
+  // half-step later (no wait on the LDS latency in between)
+  int pg_raw[GPW];
+  auto pages_load = [&](int k0) {
+#pragma unroll
+    for (int l = 0; l < GPW; ++l) {
+      const int pos = k0 + 16 * (gw + l);
+      pg_raw[l] = s_pages[min(max((min(pos, last) >> lp) - pg_lo, 0), n_pg - 1)];
+    }
+  };
+  auto pages_take = [&](int (&pg)[GPW]) {
+#pragma unroll
+    for (int l = 0; l < GPW; ++l) pg[l] = __builtin_amdgcn_readfirstlane(pg_raw[l]);
   };
   auto issue = [&](int stage, int k0, const int (&pg)[GPW]) {
     if (k_wave) {
@@ -454,7 +479,7 @@ void attn_bf16_kernel(Params p) {
     }
     rescale = __any(need);
   };
-  // ---- probabilities of a tile (bf16 B operand of the PV product), l update
+  // ---- probabilities of a tile (bf16 B operand of the PV product)
   auto probs = [&](f32x4 (&sacc)[RW][4], bf16x8 (&pf)[RW][2]) {
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
@@ -462,15 +487,12 @@ void attn_bf16_kernel(Params p) {
       float part[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        part[t] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r][t][i], p.scale_log2, -m_use));
-          sacc[r][t][i] = e;
-          part[t] += e;
-        }
+        for (int i = 0; i < 4; ++i)
+          sacc[r][t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r][t][i], p.scale_log2, -m_use));
+        part[t] = (sacc[r][t][0] + sacc[r][t][1]) + (sacc[r][t][2] + sacc[r][t][3]);
       }
-      l_run[r] = l_run[r] * alpha[r] + row_sum4((part[0] + part[1]) + (part[2] + part[3]));
+      l_lane[r] += (part[0] + part[1]) + (part[2] + part[3]);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         bf16x8 f;
@@ -562,9 +584,11 @@ void attn_bf16_kernel(Params p) {
     row_update(sc);
     if (rescale) {
 #pragma unroll
-      for (int r = 0; r < RW; ++r)
+      for (int r = 0; r < RW; ++r) {
 #pragma unroll
         for (int u = 0; u < DU; ++u) o[r][u] *= alpha[r];
+        l_lane[r] *= alpha[r];
+      }
     }
     probs(sc, pf);
   };
@@ -593,15 +617,17 @@ void attn_bf16_kernel(Params p) {
   }
   int m = 0;
   // start of slot 2m: tile m has landed and is visible, tile m+2 requested
+  int c_n3 = ke;
   auto head = [&]() {
     if (c_cur < ke) wait_vm(c_n1 < ke ? IPW : 0);
     barrier();
     if (c_cur < ke) zero_tail(m & (STAGES - 1), c_cur);
     if (c_n2 < ke) issue((m + 2) & (STAGES - 1), c_n2, pgn);
+    c_n3 = next_tile(c_n2);
+    pages_load(c_n3);
   };
   auto advance = [&]() {
-    const int c_n3 = next_tile(c_n2);
-    pages_for(c_n3, pgn);
+    pages_take(pgn);
     c_prev = c_cur; c_cur = c_n1; c_n1 = c_n2; c_n2 = c_n3;
     ++m;
   };
@@ -641,6 +667,9 @@ void attn_bf16_kernel(Params p) {
 
   // ---- epilogue: lane (r16, q4) holds O[row r16][16u + 4q4 + i]
   const size_t R_tot = (size_t)p.total_nodes * p.hq;
+  float l_run[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) l_run[r] = row_sum4(l_lane[r]);
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     if (!row_ok[r]) continue;
@@ -659,65 +688,59 @@ void attn_bf16_kernel(Params p) {
       const size_t prow = (size_t)split * R_tot + orow[r];
 #pragma unroll
       for (int u = 0; u < DU; ++u)
-        *reinterpret_cast<f32x4*>(p.part_o + prow * D + 16 * u + 4 * q4) = o[r][u];
-      if (q4 == 0) *reinterpret_cast<float2*>(p.part_ml + prow * 2) = float2{m_run[r], l_run[r]};
+        __builtin_nontemporal_store(o[r][u], reinterpret_cast<f32x4*>(p.part_o + prow * D + 16 * u + 4 * q4));
+      if (q4 == 0) {
+        __builtin_nontemporal_store(m_run[r], p.part_ml + prow * 2);
+        __builtin_nontemporal_store(l_run[r], p.part_ml + prow * 2 + 1);
+      }
     }
   }
 }
 
 // Merge of split partials: m = max m_s, l = sum 2^(m_s - m) l_s,
-// o = sum 2^(m_s - m) o_s / l, lse = (m + log2 l) ln 2. One row per D/4 lanes.
+// o = sum 2^(m_s - m) o_s / l, lse = (m + log2 l) ln 2. One row per D/4
+// lanes; the partials of 16 splits are loaded at once (one round trip), and
+// longer split lists are folded in chunks with the same online rescaling.
+// Every (split, row) pair holds a partial or an empty marker (m = -inf),
+// whose o is never read into the sums.
 template <int D, typename OutT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
-                                                      const int32_t* __restrict__ cu_nodes,
-                                                      const int32_t* __restrict__ prefix_len,
-                                                      int32_t batch, int32_t total_nodes, int32_t hq,
-                                                      int32_t splits, int32_t keys_per_split,
+                                                      int64_t R_tot, int32_t splits,
                                                       OutT* __restrict__ out, float* __restrict__ lse) {
   constexpr int LPR = D / 4;               // lanes per row
   constexpr int RPB = 256 / LPR;           // rows per block
-  const size_t R_tot = (size_t)total_nodes * hq;
-  const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  constexpr int CH = 16;                   // splits per chunk
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   const int sub = threadIdx.x % LPR;
   if (row >= R_tot) return;
-  const int node = (int)(row / hq);
-  int lo = 0, hi = batch;  // request b with cu_nodes[b] <= node < cu_nodes[b+1]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu_nodes[mid] <= node) lo = mid; else hi = mid;
-  }
-  const int b = lo;
-  const int kv_end = max(prefix_len[b], 0) + (cu_nodes[b + 1] - cu_nodes[b]);
-  const int ns = min(splits, (kv_end + keys_per_split - 1) / keys_per_split);
-  // pass 1: the split maxima (independent loads, 8 in flight)
-  float m = -INFINITY;
-  for (int s0 = 0; s0 < ns; s0 += 8) {
-    float ms[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      ms[j] = (s0 + j < ns) ? part_ml[((size_t)(s0 + j) * R_tot + row) * 2] : -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, ms[j]);
-  }
-  // pass 2: weighted sums of l and o
-  float l = 0.f;
+  float m = -INFINITY, l = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < ns; s0 += 8) {
-    float2 ml[8];
-    f32x4 os[8];
+  for (int s0 = 0; s0 < splits; s0 += CH) {
+    float2 ml[CH];
+    f32x4 os[CH];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const size_t pr = (size_t)(s0 + j) * R_tot + row;
-      ml[j] = (s0 + j < ns) ? *reinterpret_cast<const float2*>(part_ml + pr * 2) : float2{-INFINITY, 0.f};
-      os[j] = (s0 + j < ns) ? *reinterpret_cast<const f32x4*>(part_o + pr * D + 4 * sub) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < CH; ++j) {
+      const int64_t pr = (int64_t)(s0 + j) * R_tot + row;
+      const bool ok = s0 + j < splits;
+      ml[j] = ok ? *reinterpret_cast<const float2*>(part_ml + pr * 2) : float2{-INFINITY, 0.f};
+      os[j] = ok ? *reinterpret_cast<const f32x4*>(part_o + pr * D + 4 * sub) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    float mc = m;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float w = (ml[j].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml[j].x - m);
+    for (int j = 0; j < CH; ++j) mc = fmaxf(mc, ml[j].x);
+    if (mc == -INFINITY) continue;
+    const float a = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mc);
+    l *= a;
+    acc *= a;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const bool live = ml[j].x != -INFINITY;
+      const float w = live ? __builtin_amdgcn_exp2f(ml[j].x - mc) : 0.f;
       l += w * ml[j].y;
-      acc += w * os[j];
+      acc = live ? acc + w * os[j] : acc;
     }
+    m = mc;
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
   OutT* dst = out + row * D + 4 * sub;
@@ -956,12 +979,10 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t stre
   const int cgrid = (int)((rtot + rpb - 1) / rpb);
   if (a.head_dim == 64)
     hipLaunchKernelGGL((combine_kernel<64, __bf16>), dim3(cgrid), dim3(256), 0, stream, p.part_o,
-                       p.part_ml, a.cu_nodes, a.prefix_len, a.batch, a.total_nodes, a.hq,
-                       plan.splits, plan.keys_per_split, p.out, a.lse);
+                       p.part_ml, (int64_t)rtot, plan.splits, p.out, a.lse);
   else
     hipLaunchKernelGGL((combine_kernel<128, __bf16>), dim3(cgrid), dim3(256), 0, stream, p.part_o,
-                       p.part_ml, a.cu_nodes, a.prefix_len, a.batch, a.total_nodes, a.hq,
-                       plan.splits, plan.keys_per_split, p.out, a.lse);
+                       p.part_ml, (int64_t)rtot, plan.splits, p.out, a.lse);
   return hipGetLastError();
 }
 
