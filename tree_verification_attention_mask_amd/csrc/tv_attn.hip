@@ -52,6 +52,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kTile = 64;     // keys per tile
 constexpr int kNumCUs = 256;  // MI355X compute units (the launch plan targets one pass over them)
 constexpr int kMaxSplitPages = 4096;  // page ids one workgroup can stage (16-token pages: 64K keys)
+constexpr int kMaxLptBatch = 256;   // requests the in-kernel longest-first order handles
 constexpr float kLazyMax = 8.f;      // running-max slack before O is rescaled (log2 units)
 
 struct Params {
@@ -69,6 +70,7 @@ struct Params {
   int32_t num_pages, max_pages, batch, total_nodes;
   int32_t hq, hkv, group, page_size;
   int32_t row_blocks, splits, keys_per_split;
+  int32_t lpt;       // map block order onto requests longest first (batch <= kMaxLptBatch)
   float scale_log2;  // softmax scale * log2(e), > 0
 };
 
@@ -159,6 +161,7 @@ void attn_bf16_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) __bf16 sV[STAGES][TILE_E];
   __shared__ int s_pages[kMaxSplitPages];  // page ids of this block's key window
   __shared__ int s_bounds[4];
+  __shared__ int s_len[kMaxLptBatch], s_order[kMaxLptBatch];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
@@ -172,8 +175,30 @@ void attn_bf16_kernel(Params p) {
   wg /= p.splits;
   const int g = wg % p.hkv;
   wg /= p.hkv;
-  const int b = wg % p.batch;
+  int b = wg % p.batch;
   const int rb = p.row_blocks - 1 - wg / p.batch;
+  if (p.lpt) {
+    // Longest-first: when the grid takes several rounds of the CUs, blocks
+    // of long requests are dispatched first (ranked by key count, ties by
+    // index), so that short ones fill the tail. Each block ranks the batch
+    // itself; this costs one dependent load before the page table.
+    for (int i = tid; i < p.batch; i += T) {
+      const int c0 = clampi(p.cu_nodes[i], 0, p.total_nodes);
+      s_len[i] = max(p.prefix_len[i], 0) + clampi(p.cu_nodes[i + 1], c0, p.total_nodes) - c0;
+    }
+    __syncthreads();
+    for (int i = tid; i < p.batch; i += T) {
+      const int li = s_len[i];
+      int rank = 0;
+      for (int j = 0; j < p.batch; ++j) {
+        const int lj = s_len[j];
+        rank += (lj > li || (lj == li && j < i)) ? 1 : 0;
+      }
+      s_order[rank] = i;
+    }
+    __syncthreads();
+    b = s_order[b];
+  }
   const int ks = split * p.keys_per_split;
 
   // Page ids of the split's key window [ks, ks + keys_per_split + 64): their
@@ -534,7 +559,8 @@ void attn_bf16_kernel(Params p) {
   // loads of tile m, then the barrier makes every wave's loads visible.
   // wait until at most `pending` loads of this wave are in flight
   auto wait_vm = [&](int pending) {
-    if (pending >= IPW) wait_vmem<IPW>();
+    if (pending >= 2 * IPW) wait_vmem<2 * IPW>();
+    else if (pending >= IPW) wait_vmem<IPW>();
     else wait_vmem<0>();
   };
   auto barrier = [&]() {
@@ -603,32 +629,57 @@ void attn_bf16_kernel(Params p) {
   // loads stay in flight)
   __builtin_amdgcn_s_waitcnt(W_ALL & ~0x0F00);
   barrier();
+  // Solo blocks: the waves of group B hold no rows (at most 16*NW/2 rows),
+  // so only group A reads the tiles and the stage of tile m-1 is free once
+  // slot 2m ends. Tiles are then requested three ahead, in slot 2m+1, into
+  // that stage (3 tiles in flight instead of 2: these blocks are bound by
+  // HBM latency, not by the matrix cores).
+  const bool solo = (NW == 4) || (rows - row0 <= 16 * (NW / 2));
+  int c_n3 = solo ? next_tile(c_n2) : ke;  // tile to request in slot 2m+1 (solo)
   int pgn[GPW];
   if (c_cur < ke) { pages_for(c_cur, pgn); issue(0, c_cur, pgn); }
   if (c_n1 < ke) { pages_for(c_n1, pgn); issue(1, c_n1, pgn); }
-  pages_for(c_n2, pgn);
   // Q fragments and mask rows are used from registers from here on (this
-  // waits for them, and for the two tiles just requested)
+  // waits for them, and for the tiles just requested)
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     asm volatile("" : "+v"(m_w0[r]), "+v"(m_w1[r]));
 #pragma unroll
     for (int s = 0; s < DS; ++s) asm volatile("" : "+v"(qf[r][s]));
   }
+  if (solo) {
+    if (c_n2 < ke) { pages_for(c_n2, pgn); issue(2, c_n2, pgn); }
+    pages_for(c_n3, pgn);
+  } else {
+    pages_for(c_n2, pgn);
+  }
   int m = 0;
-  // start of slot 2m: tile m has landed and is visible, tile m+2 requested
-  int c_n3 = ke;
+  // start of slot 2m: tile m has landed and is visible; tile m+2 is
+  // requested now (tile m+3 in slot 2m+1 for solo blocks)
+  int c_nn = ke;  // successor of the tile requested in this step
   auto head = [&]() {
-    if (c_cur < ke) wait_vm(c_n1 < ke ? IPW : 0);
+    if (c_cur < ke)
+      wait_vm(solo ? (c_n2 < ke ? 2 * IPW : (c_n1 < ke ? IPW : 0)) : (c_n1 < ke ? IPW : 0));
     barrier();
     if (c_cur < ke) zero_tail(m & (STAGES - 1), c_cur);
-    if (c_n2 < ke) issue((m + 2) & (STAGES - 1), c_n2, pgn);
-    c_n3 = next_tile(c_n2);
-    pages_load(c_n3);
+    if (!solo) {
+      if (c_n2 < ke) issue((m + 2) & (STAGES - 1), c_n2, pgn);
+      c_nn = next_tile(c_n2);
+      pages_load(c_nn);
+    }
+  };
+  auto mid = [&]() {  // after the barrier that opens slot 2m+1
+    if (solo) {
+      if (c_n3 < ke) issue((m + 3) & (STAGES - 1), c_n3, pgn);
+      c_nn = next_tile(c_n3);
+      pages_load(c_nn);
+    }
   };
   auto advance = [&]() {
     pages_take(pgn);
-    c_prev = c_cur; c_cur = c_n1; c_n1 = c_n2; c_n2 = c_n3;
+    // value selects (a conditional store would take the variables' address)
+    const int n2 = solo ? c_n3 : c_nn, n3 = solo ? c_nn : c_n3;
+    c_prev = c_cur; c_cur = c_n1; c_n1 = c_n2; c_n2 = n2; c_n3 = n3;
     ++m;
   };
   // Each group runs a straight loop (no per-slot branch between the two
@@ -639,6 +690,7 @@ void attn_bf16_kernel(Params p) {
       head();
       cluster_m(m);
       barrier();
+      mid();
       cluster_v(c_cur);
       advance();
     }
@@ -649,6 +701,7 @@ void attn_bf16_kernel(Params p) {
     if (c_cur < ke) {
       head();
       barrier();
+      mid();
       cluster_m(m);
       advance();
     }
@@ -656,6 +709,7 @@ void attn_bf16_kernel(Params p) {
       head();
       cluster_v(c_prev);
       barrier();
+      mid();
       cluster_m(m);
       advance();
     }
@@ -972,6 +1026,7 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t stre
   p.keys_per_split = plan.keys_per_split;
   p.scale_log2 = a.scale * kLog2e;
   const int grid = a.batch * a.hkv * plan.row_blocks * plan.splits;
+  p.lpt = (a.batch >= 2 && a.batch <= kMaxLptBatch && grid > kNumCUs) ? 1 : 0;
   hipError_t e = (a.head_dim == 64) ? dispatch_bf16<64>(p, plan, grid, stream)
                                     : dispatch_bf16<128>(p, plan, grid, stream);
   if (e != hipSuccess || plan.splits == 1) return e;
