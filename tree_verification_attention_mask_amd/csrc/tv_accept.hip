@@ -25,9 +25,10 @@ __global__ __launch_bounds__(64) void accept_kernel(
     const int32_t* __restrict__ target_tok, const int32_t* __restrict__ cu_nodes,
     int32_t total_nodes, int32_t cap, int32_t max_depth, int32_t* __restrict__ accept_len,
     int32_t* __restrict__ path, int32_t* __restrict__ bonus_tok) {
-  extern __shared__ int32_t lds[];  // parent[cap], state[cap]
+  extern __shared__ int32_t lds[];  // parent[cap], state[cap], target[cap]
   int32_t* s_par = lds;
   int32_t* s_state = lds + cap;
+  int32_t* s_tgt = lds + 2 * cap;
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
   const int n0 = clampi(cu_nodes[b], 0, total_nodes);
@@ -40,7 +41,13 @@ __global__ __launch_bounds__(64) void accept_kernel(
     // clamp malformed parents into [0, i) so every walk moves strictly upward
     int p = live ? parent[n0 + i] : -1;
     p = (i == 0) ? -1 : clampi(p, 0, i - 1);
-    const bool match = live && (i == 0 || draft_tok[n0 + i] == target_tok[n0 + p]);
+    // every node's target token is loaded once, with its parent and draft
+    // token; a child reads its parent's from a lane (same chunk) or from LDS
+    const int tgt = live ? target_tok[n0 + i] : -1;
+    const int dft = live ? draft_tok[n0 + i] : 0;
+    const int tp_lane = __shfl(tgt, (p >= c0) ? p - c0 : lane, 64);
+    const int tp = (p >= c0) ? tp_lane : (p >= 0 ? s_tgt[p] : -1);
+    const bool match = live && (i == 0 || dft == tp);
     // (ok, d, link): ok/d cover the path from i up to (excluding) lane link
     int ok, d, link;
     if (!live || i == 0) {
@@ -60,7 +67,7 @@ __global__ __launch_bounds__(64) void accept_kernel(
       if (link >= 0) { ok &= ok2; d += d2; link = l2; }
     }
     const int state = ok ? d : -1;
-    if (live) { s_par[i] = p; s_state[i] = state; }
+    if (live) { s_par[i] = p; s_state[i] = state; s_tgt[i] = tgt; }
     if (live && state >= 0)
       best_key = max(best_key, (state << kIdxBits) | ((1 << kIdxBits) - 1 - i));
     __syncthreads();
@@ -79,7 +86,7 @@ __global__ __launch_bounds__(64) void accept_kernel(
   for (int t = lane; t <= max_depth; t += 64) prow[t] = (n > 0 && t <= best_depth) ? s_state[t] : -1;
   if (lane == 0) {
     accept_len[b] = best_depth;
-    if (bonus_tok) bonus_tok[b] = n > 0 ? target_tok[n0 + best] : -1;
+    if (bonus_tok) bonus_tok[b] = n > 0 ? s_tgt[best] : -1;
   }
 }
 
@@ -90,12 +97,12 @@ hipError_t launch_accept(const int32_t* parent, const int32_t* draft_tok, const 
                          int32_t max_nodes, int32_t max_depth, int32_t* accept_len, int32_t* path,
                          int32_t* bonus_tok, hipStream_t stream) {
   const int cap = max_nodes < 1 ? 1 : max_nodes;
-  const size_t lds = 2 * sizeof(int32_t) * (size_t)cap;
+  const size_t lds = 3 * sizeof(int32_t) * (size_t)cap;
   static bool lds_raised = false;  // allow > 64 KiB dynamic LDS for the largest trees
   if (!lds_raised) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&accept_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(2 * sizeof(int32_t) * TV_MAX_ACCEPT_NODES));
+                                       (int)(3 * sizeof(int32_t) * TV_MAX_ACCEPT_NODES));
     if (e != hipSuccess) return e;
     lds_raised = true;
   }

@@ -7,7 +7,8 @@
 //
 // One workgroup per request. BITS form: every node's ancestor set is built
 // by pointer jumping in LDS (round k doubles the covered path length), so the
-// number of rounds is ceil(log2(depth)) whatever the tree's shape. ANCHOR
+// number of rounds is ceil(log2(depth)) whatever the tree's shape; trees of
+// at most 64 nodes use one wavefront and lane shuffles instead. ANCHOR
 // form: the trunk length is a block-wide min, and each branch node finds its
 // branch start with a block-wide running-max scan.
 #include "tv_internal.h"
@@ -107,6 +108,48 @@ __global__ __launch_bounds__(kMaskThreads) void mask_bits_kernel(
   if (threadIdx.x == 0) err[b] = 0;
 }
 
+// Trees that fit one mask word (<= 64 nodes): one wavefront per request,
+// lane i owns node i. Validation is one ballot; the ancestor sets are built
+// by the same pointer jumping as above, over the lanes with shuffles (at most
+// 6 rounds), so there is no LDS and no barrier.
+constexpr int kWavesPerBlock = 4;
+__global__ __launch_bounds__(64 * kWavesPerBlock) void mask_bits1_kernel(
+    const int32_t* __restrict__ parent, const int32_t* __restrict__ cu_nodes, int32_t batch,
+    int32_t total_nodes, uint64_t* __restrict__ bits, int32_t* __restrict__ depth,
+    int32_t* __restrict__ err) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (b >= batch) return;
+  const int n0 = clampi(cu_nodes[b], 0, total_nodes);
+  const int n = clampi(cu_nodes[b + 1], n0, total_nodes) - n0;
+  const bool live = lane < n;
+  const int p = live ? parent[n0 + lane] : -1;
+  const bool viol = live && ((lane == 0) ? (p != -1) : (p < 0 || p >= lane));
+  if (n <= 0 || n > 64 || __ballot(viol) != 0) {
+    for (int i = lane; i < n; i += 64) {
+      bits[n0 + i] = 0ull;
+      depth[n0 + i] = -1;
+    }
+    if (lane == 0) err[b] = 1;
+    return;
+  }
+  // bits(i) = {i, parent(i)}, jump(i) = parent(i); then
+  // bits(i) |= bits(jump(i)), jump(i) = jump(jump(i)) until every jump is -1
+  uint64_t m = live ? ((1ull << lane) | (p >= 0 ? (1ull << p) : 0ull)) : 0ull;
+  int j = p;
+  while (__any(j >= 0)) {
+    const int src = j >= 0 ? j : lane;
+    const uint64_t mj = __shfl(m, src, 64);
+    const int jj = __shfl(j, src, 64);
+    if (j >= 0) { m |= mj; j = jj; }
+  }
+  if (live) {
+    bits[n0 + lane] = m;
+    depth[n0 + lane] = __popcll(m) - 1;
+  }
+  if (lane == 0) err[b] = 0;
+}
+
 // Block-wide inclusive running max over one value per thread (256 threads).
 __device__ int block_scan_max(int v, int* wave_tot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -190,6 +233,12 @@ __global__ __launch_bounds__(kMaskThreads) void mask_anchor_kernel(
 hipError_t launch_mask_bits(const int32_t* parent, const int32_t* cu_nodes, int32_t batch,
                             int32_t total_nodes, int32_t words, uint64_t* bits, int32_t* depth,
                             int32_t* err, hipStream_t stream) {
+  if (words == 1) {
+    const int grid = (batch + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL(mask_bits1_kernel, dim3(grid), dim3(64 * kWavesPerBlock), 0, stream, parent,
+                       cu_nodes, batch, total_nodes, bits, depth, err);
+    return hipGetLastError();
+  }
   const size_t cap = 64 * (size_t)words;
   const size_t lds = cap * words * sizeof(uint64_t) + cap * sizeof(int32_t);
   static bool lds_raised = false;  // allow > 64 KiB dynamic LDS (words > 11)
