@@ -11,4 +11,5 @@ from .oracle import (  # noqa: F401
     mask_anchor,
     tree_attn,
     accept,
+    dcut_select,
 )

@@ -55,6 +55,8 @@ def _load():
         lib.orc_tree_attn.restype = ctypes.c_int
         lib.orc_accept.argtypes = [P, P, P, P, I, I, P, P, P]
         lib.orc_accept.restype = None
+        lib.orc_dcut_select.argtypes = [P, P, I, I, I, P, P, P, P]
+        lib.orc_dcut_select.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -160,3 +162,24 @@ def accept(parent, draft_tok, target_tok, cu_nodes, max_depth: int):
     lib.orc_accept(_p(par), _p(dr), _p(tg), _p(cu), batch, max_depth, _p(al), _p(path),
                    _p(bonus))
     return al, path, bonus
+
+
+def dcut_select(conf, tokens, budget: int):
+    """D-cut selection: ``conf`` float32 [B, D], ``tokens`` int32 [B, D+1].
+
+    Returns (n_keep [B], cu_nodes [B+1], parent [budget], packed_tokens [budget]),
+    int32; raises ValueError on a budget outside [B, B*(D+1)].
+    """
+    lib = _load()
+    conf = _np(conf, np.float32)
+    tok = _np(tokens, np.int32)
+    batch, d = conf.shape
+    assert tok.shape == (batch, d + 1)
+    n_keep = np.zeros(batch, np.int32)
+    cu = np.zeros(batch + 1, np.int32)
+    par = np.zeros(max(budget, 1), np.int32)
+    ptok = np.zeros(max(budget, 1), np.int32)
+    if lib.orc_dcut_select(_p(conf), _p(tok), batch, d, int(budget), _p(n_keep), _p(cu),
+                           _p(par), _p(ptok)) != 0:
+        raise ValueError("budget must lie in [batch, batch * (draft_len + 1)]")
+    return n_keep, cu, par[:budget], ptok[:budget]

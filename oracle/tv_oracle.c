@@ -8,6 +8,9 @@
  * Everything here is the definition written out, one row / one node at a time,
  * in double precision (inputs are float32 arrays that hold exactly the values
  * the GPU receives; bf16 inputs are upcast exactly before they get here).
+ * One exception: the D-cut scores decide an integer (which positions are
+ * kept), so they are formed in fp32, in the same order the library forms
+ * them, and the decision is taken on those values.
  *
  * Sources (the four web pages on candidate-tree speculative decoding):
  *   [Graft]      Graft, arXiv:2605.20104 (163.com article "浙江大学、阿里巴巴联手破解AI推理瓶颈")
@@ -312,4 +315,62 @@ void orc_accept(const int32_t* parent, const int32_t* draft_tok,
     for (int j = best, t = best_depth; j != -1; j = par[j], --t)
       if (t <= max_depth) prow[t] = j;
   }
+}
+
+/* ------------------------------------------------------------------------ */
+/* D-cut verification budget.                                                */
+/* [D-cut] technical summary §2, cross-request pruning and the pipeline's    */
+/* scoring & ranking and packing steps: each draft position is scored by the */
+/* product of the draft confidences up to it (the chance the block survives  */
+/* to that depth); all positions of the batch are ranked together, the best  */
+/* ones are verified, and since scores only fall along a block each request  */
+/* keeps a prefix, packed densely. Position 0 of every request (its current  */
+/* token) is always verified; the other budget - batch slots are ranked.     */
+/* Ties: smaller request, then smaller position. Returns 1 on a bad budget.  */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  float s;
+  int32_t b, k;
+} orc_dcut_pos;
+
+static int orc_dcut_cmp(const void* x, const void* y) {
+  const orc_dcut_pos* a = (const orc_dcut_pos*)x;
+  const orc_dcut_pos* c = (const orc_dcut_pos*)y;
+  if (a->s != c->s) return a->s > c->s ? -1 : 1;
+  if (a->b != c->b) return a->b < c->b ? -1 : 1;
+  return a->k < c->k ? -1 : (a->k > c->k);
+}
+
+int orc_dcut_select(const float* conf, const int32_t* tokens, int32_t batch,
+                    int32_t draft_len, int32_t budget, int32_t* n_keep, int32_t* cu_nodes,
+                    int32_t* parent, int32_t* packed_tokens) {
+  const int D = draft_len;
+  if (batch < 1 || D < 1 || budget < batch || budget > batch * (D + 1)) return 1;
+  orc_dcut_pos* pos = (orc_dcut_pos*)malloc(sizeof(orc_dcut_pos) * (size_t)batch * D);
+  for (int b = 0; b < batch; ++b) {
+    float s = 1.0f;                       /* position 0: the empty product */
+    for (int k = 1; k <= D; ++k) {
+      float c = conf[(size_t)b * D + (k - 1)];
+      if (!(c > 0.0f)) c = 0.0f;          /* a probability: NaN and negatives -> 0 */
+      if (c > 1.0f) c = 1.0f;
+      s = s * c;                          /* fp32, left to right along the block */
+      orc_dcut_pos* e = &pos[(size_t)b * D + (k - 1)];
+      e->s = s; e->b = b; e->k = k;
+    }
+  }
+  qsort(pos, (size_t)batch * D, sizeof(orc_dcut_pos), orc_dcut_cmp);
+  for (int b = 0; b < batch; ++b) n_keep[b] = 1;
+  for (int r = 0; r < budget - batch; ++r) n_keep[pos[r].b] += 1;
+  free(pos);
+  int off = 0;
+  for (int b = 0; b < batch; ++b) {
+    cu_nodes[b] = off;
+    for (int k = 0; k < n_keep[b]; ++k) {
+      parent[off + k] = k - 1;
+      packed_tokens[off + k] = tokens[(size_t)b * (D + 1) + k];
+    }
+    off += n_keep[b];
+  }
+  cu_nodes[batch] = off;
+  return 0;
 }

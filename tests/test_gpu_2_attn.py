@@ -72,6 +72,27 @@ def test_random_trees_many_words(n, prefix):
     _run_and_check(w, "random n=%d P=%d" % (n, prefix))
 
 
+def test_many_ragged_requests_longest_first():
+    """40 requests x 8 kv heads = 320 blocks (more than one round of the CUs):
+    blocks are mapped onto requests longest first; every request still gets
+    exactly its own rows."""
+    rng = np.random.default_rng(40)
+    trees = [W.random_tree(rng, int(rng.integers(1, 17)), max_children=2) for _ in range(40)]
+    prefix = [int(x) for x in rng.integers(0, 500, size=40)]
+    w = W.build_workload("lpt", trees, prefix, 32, 8, 128, "bf16", rng, permute_pages=True,
+                         tokens=False)
+    _run_and_check(w, "40 ragged requests")
+
+
+def test_batch_above_the_longest_first_limit():
+    """300 requests (beyond the 256 the in-kernel ranking handles): plain order."""
+    rng = np.random.default_rng(300)
+    trees = [W.random_tree(rng, int(rng.integers(1, 4))) for _ in range(300)]
+    prefix = [int(x) for x in rng.integers(0, 70, size=300)]
+    w = W.build_workload("big batch", trees, prefix, 4, 1, 64, "bf16", rng, tokens=False)
+    _run_and_check(w, "300 requests")
+
+
 @pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (16, 1, 64), (12, 4, 64), (4, 2, 128)])
 def test_head_layouts(hq, hkv, d):
     rng = np.random.default_rng(hq * 100 + hkv)

@@ -24,6 +24,13 @@ MUTANTS = {
     "depth_off_by_one": ("      int d = -1;\n", "      int d = 0;\n"),
     "anchor_depth_reset": ("branch_depth[n0 + i] = branch_depth[n0 + i - 1] + 1;",
                            "branch_depth[n0 + i] = 1;"),
+    "dcut_tie_to_larger_request": ("if (a->b != c->b) return a->b < c->b ? -1 : 1;",
+                                   "if (a->b != c->b) return a->b > c->b ? -1 : 1;"),
+    "dcut_roots_not_reserved": ("for (int r = 0; r < budget - batch; ++r)",
+                                "for (int r = 0; r < budget - batch - 1; ++r)"),
+    "dcut_no_upper_clamp": ("      if (c > 1.0f) c = 1.0f;\n", ""),
+    "dcut_score_ascending": ("if (a->s != c->s) return a->s > c->s ? -1 : 1;",
+                             "if (a->s != c->s) return a->s < c->s ? -1 : 1;"),
     "second_root_accepted": ("if (par[i] < 0 || par[i] >= i) return 1;",
                              "if (par[i] < -1 || par[i] >= i) return 1;"),
 }

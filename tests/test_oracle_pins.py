@@ -382,3 +382,100 @@ def test_repeated_sibling_tokens_pick_deepest_then_smallest_index(oracle_lib):
     tg2 = [7, 0, 9, 0]
     al2, path2, _ = oracle.accept(par2, dr2, tg2, [0, 4], 3)
     assert al2[0] == 2 and path2[0, :3].tolist() == [0, 2, 3]
+
+
+# ---------------------------------------------------------------------------
+# D-cut selection (D-cut technical summary §2: prefix-product scores, one
+# global ranking over the batch, kept positions packed as per-request prefixes)
+
+def _dcut(conf, budget, tokens=None):
+    conf = np.asarray(conf, np.float32)
+    b, d = conf.shape
+    if tokens is None:
+        tokens = np.arange(b * (d + 1), dtype=np.int32).reshape(b, d + 1)
+    return oracle.dcut_select(conf, tokens, budget)
+
+
+def test_dcut_extreme_budgets(oracle_lib):
+    rng = np.random.default_rng(1)
+    conf = rng.uniform(0.1, 1.0, size=(5, 7))
+    n, cu, par, tok = _dcut(conf, 5)                       # only the current tokens
+    assert n.tolist() == [1] * 5 and cu.tolist() == list(range(6)) and par.tolist() == [-1] * 5
+    n, cu, par, tok = _dcut(conf, 5 * 8)                   # every drafted token
+    assert n.tolist() == [8] * 5
+    for bad in (4, 41):
+        with pytest.raises(ValueError):
+            _dcut(conf, bad)
+
+
+@pytest.mark.parametrize("budget", [9, 12, 13, 20, 31])
+def test_dcut_equal_confidences_fill_depth_by_depth(oracle_lib, budget):
+    # equal confidences: the score depends on depth only, so the extra slots
+    # go one depth at a time, requests in order (closed form)
+    B, D = 6, 5
+    n = _dcut(np.full((B, D), 0.75), budget)[0]
+    q, r = divmod(budget - B, B)
+    assert n.tolist() == [1 + q + (b < r) for b in range(B)]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_dcut_keeps_the_best_prefix_set_by_brute_force(oracle_lib, seed):
+    # among all per-request prefix lengths with the same total, the kept set
+    # has the largest total score (scores distinct here, so it is unique)
+    import itertools
+    rng = np.random.default_rng(seed)
+    B, D = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+    conf = rng.uniform(0.05, 1.0, size=(B, D)).astype(np.float32)
+    score = np.ones((B, D + 1), np.float64)
+    score[:, 1:] = np.cumprod(conf, axis=1, dtype=np.float32)
+    for budget in range(B, B * (D + 1) + 1):
+        best, arg = -1.0, None
+        for ns in itertools.product(range(1, D + 2), repeat=B):
+            if sum(ns) != budget:
+                continue
+            tot = sum(score[b, :ns[b]].sum() for b in range(B))
+            if tot > best + 1e-12:
+                best, arg = tot, ns
+        assert _dcut(conf, budget)[0].tolist() == list(arg)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_dcut_one_more_slot_adds_one_position(oracle_lib, seed):
+    rng = np.random.default_rng(100 + seed)
+    conf = rng.beta(4.0, 2.0, size=(9, 15))
+    prev = _dcut(conf, 9)[0]
+    for budget in range(10, 9 * 16 + 1):
+        cur = _dcut(conf, budget)[0]
+        diff = cur - prev
+        assert diff.min() == 0 and diff.sum() == 1
+        prev = cur
+
+
+def test_dcut_agrees_with_the_config3_recipe(oracle_lib):
+    # the config-3 generator ranks the same scores in float64 with its own sort;
+    # away from near-ties both give the same per-request lengths
+    w = W.make(3)
+    conf = np.asarray(w.meta["confidence"], np.float64)
+    n = _dcut(conf.astype(np.float32), w.meta["budget"])[0]
+    assert n.tolist() == [int(x) for x in w.nodes_per_request]
+
+
+def test_dcut_confidences_are_probabilities(oracle_lib):
+    # NaN / negative -> 0 and > 1 -> 1: a 0 ends a block's scores, a 1 keeps them
+    conf = np.array([[np.nan, 0.9, 0.9], [1.5, 0.6, 0.5], [-2.0, 1.0, 1.0], [0.8, 0.1, 0.1]],
+                    np.float32)
+    n = _dcut(conf, 4 + 2)[0]
+    # request 1 scores 1.0, 0.6, 0.3 (not 1.5, 0.9, ...), request 3 0.8, 0.08, ...
+    assert n.tolist() == [1, 2, 1, 2]
+
+
+def test_dcut_packs_prefixes_in_request_order(oracle_lib):
+    rng = np.random.default_rng(7)
+    conf = rng.uniform(0.2, 1.0, size=(4, 6))
+    tokens = rng.integers(0, 10 ** 6, size=(4, 7)).astype(np.int32)
+    n, cu, par, tok = _dcut(conf, 15, tokens)
+    assert cu.tolist() == [0] + np.cumsum(n).tolist()
+    for b in range(4):
+        seg = slice(cu[b], cu[b + 1])
+        assert tok[seg].tolist() == tokens[b, :n[b]].tolist()
+        assert par[seg].tolist() == list(range(-1, n[b] - 1))
