@@ -234,8 +234,11 @@ def main():
     g_attn = capture(lambda: [attn_call(s, mask_out | {"kind": w.mask_kind,
                                                       "words_per_node": m["words_per_node"]})
                               for s in range(R)])
-    g_mask = capture(lambda: [mask_call() for _ in range(R)])
-    g_acc = capture(lambda: [accept_call() for _ in range(R)]) if has_tok else None
+    # the small calls read the same few KB every time: a graph of at least 32
+    # back-to-back calls keeps graph-launch overhead out of their figures
+    RS = max(R, 32)
+    g_mask = capture(lambda: [mask_call() for _ in range(RS)])
+    g_acc = capture(lambda: [accept_call() for _ in range(RS)]) if has_tok else None
     # a replay reproduces the eager results bit for bit
     outs[0].zero_()
     g_full.replay()
@@ -272,8 +275,26 @@ def main():
         return a.elapsed_time(b) * 1e3 / (reps * calls_per_replay)  # us per call
 
     us_attn = time_graph(g_attn, R)
-    us_mask = time_graph(g_mask, R)
-    us_acc = time_graph(g_acc, R) if g_acc is not None else 0.0
+    us_mask = time_graph(g_mask, RS)
+    us_acc = time_graph(g_acc, RS) if g_acc is not None else 0.0
+
+    # D-cut budget selection (the step that shapes this workload's chains),
+    # timed the same way when the workload carries draft confidences
+    next_rows = {}
+    if "confidence" in (w.meta or {}):
+        conf_d = torch.from_numpy(np.asarray(w.meta["confidence"], np.float32)).to(dev)
+        tok_d = torch.zeros((conf_d.shape[0], conf_d.shape[1] + 1), dtype=torch.int32, device=dev)
+        nb, kb = conf_d.shape[0], w.meta["budget"]
+        dc_out = {"n_keep": torch.empty(nb, dtype=torch.int32, device=dev),
+                  "cu_nodes": torch.empty(nb + 1, dtype=torch.int32, device=dev),
+                  "parent": torch.empty(kb, dtype=torch.int32, device=dev),
+                  "packed_tokens": torch.empty(kb, dtype=torch.int32, device=dev)}
+        tv.dcut_select(conf_d, tok_d, kb, out=dc_out)
+        g_dcut = capture(lambda: [tv.dcut_select(conf_d, tok_d, kb, out=dc_out)
+                                  for _ in range(RS)])
+        next_rows["dcut_select_us"] = time_graph(g_dcut, RS)
+        next_rows["dcut_select_shape"] = "batch %d, draft_len %d, budget %d" % (
+            conf_d.shape[0], conf_d.shape[1], w.meta["budget"])
     achieved_gbs = alg_bytes / (us_attn * 1e-6) / 1e9
     achieved_tflops = alg_flops / (us_attn * 1e-6) / 1e12
     plan_splits = (need > 0)
@@ -309,6 +330,8 @@ def main():
         "breakdown_us": {"tree_mask_build": us_mask, "tree_verify_attn": us_attn,
                          "tree_accept": us_acc, "step": ms_per_step * 1e3},
     }
+    if next_rows:
+        result["next_rows"] = next_rows
     if not args.no_cpu_baseline:
         log("timing the CPU oracle (about %.0f s)" % args.cpu_seconds)
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

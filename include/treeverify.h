@@ -6,6 +6,9 @@
  *   2. tv_tree_verify_attn one target attention layer: every tree node attends
  *                          the request's KV prefix plus its own root path
  *   3. tv_tree_accept      greedy acceptance: longest accepted root-to-leaf path
+ * and, ahead of them for batches of chain drafts,
+ *   0. tv_dcut_select      D-cut verification budget: rank the batch's draft
+ *                          positions and pack each request's kept prefix
  *
  * Sources (four web pages on candidate-tree speculative decoding):
  *   Graft      arXiv:2605.20104 -- 163.com article "浙江大学、阿里巴巴联手破解AI推理瓶颈"
@@ -210,6 +213,40 @@ tv_status_t tv_tree_accept(const int32_t* parent, const int32_t* draft_tok,
                            int32_t total_nodes, int32_t max_nodes, int32_t max_depth,
                            int32_t* accept_len, int32_t* path, int32_t* bonus_tok,
                            hipStream_t stream);
+
+/*
+ * tv_dcut_select -- D-cut verification budget over a batch of chain drafts.
+ *
+ * D-cut technical summary §2 (cross-request pruning; pipeline: scoring and
+ * ranking, packing): each draft position is scored by the product of its
+ * block's draft confidences up to it (the chance the block survives to that
+ * depth); all positions of the batch are ranked together and the best are
+ * verified; since scores only fall along a block, every request keeps a
+ * prefix, and the kept positions are packed densely. The budget ratio and the
+ * profiled cost model that picks it stay with the caller: the call takes the
+ * number of verified positions, budget = rho * batch * (draft_len + 1).
+ *
+ * Scores: position 0 of request b (its current token) is always verified;
+ * s(b,k) = fl(s(b,k-1) * c(b,k)) in fp32 for k = 1..draft_len with s(b,0) = 1
+ * and every confidence clamped to [0, 1] (NaN -> 0). The budget - batch
+ * remaining slots go to the draft positions of largest score, ties to the
+ * smaller b, then the smaller k.
+ *
+ *   conf          [batch][draft_len] fp32; conf[b][k-1] is the confidence of drafted token k
+ *   tokens        [batch][draft_len + 1] int32: position 0 = current token, k = drafted token k
+ *   budget        (host) batch <= budget <= batch * (draft_len + 1), else TV_ERR_INVALID_ARGUMENT
+ *   n_keep        out [batch]: verified positions of request b, 1 .. draft_len + 1
+ *   cu_nodes      out [batch + 1]: exclusive scan of n_keep (cu_nodes[batch] = budget)
+ *   parent        out [budget]: the packed chain trees (-1 at each request's position 0,
+ *                 k - 1 at position k), in the layout tv_tree_mask_build takes
+ *   packed_tokens out [budget]: tokens[b][k] for the kept positions, request by request
+ * Limits: draft_len >= 1, batch * draft_len <= TV_MAX_DCUT_DRAFT_POSITIONS
+ * (TV_ERR_UNSUPPORTED beyond). One workgroup; deterministic.
+ */
+#define TV_MAX_DCUT_DRAFT_POSITIONS 32768
+tv_status_t tv_dcut_select(const float* conf, const int32_t* tokens, int32_t batch,
+                           int32_t draft_len, int32_t budget, int32_t* n_keep, int32_t* cu_nodes,
+                           int32_t* parent, int32_t* packed_tokens, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* tv_status_string(tv_status_t status);

@@ -89,6 +89,17 @@ def test_mask_and_accept_argument_checks():
     assert ac(FAKE, FAKE, FAKE, FAKE, 1, 9000, 9000, 3, FAKE, FAKE, None, None) == 2
 
 
+def test_dcut_argument_checks():
+    lib = tv.load_library()
+    ds = lib.tv_dcut_select
+    assert ds(None, FAKE, 4, 3, 8, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert ds(FAKE, FAKE, 0, 3, 8, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert ds(FAKE, FAKE, 4, 0, 8, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert ds(FAKE, FAKE, 4, 3, 3, FAKE, FAKE, FAKE, FAKE, None) == 1    # budget < batch
+    assert ds(FAKE, FAKE, 4, 3, 17, FAKE, FAKE, FAKE, FAKE, None) == 1   # budget > batch*(D+1)
+    assert ds(FAKE, FAKE, 4097, 8, 5000, FAKE, FAKE, FAKE, FAKE, None) == 2  # > 32768 positions
+
+
 def test_product_path_never_touches_the_oracle():
     pkg = os.path.join(ROOT, "tree_verification_attention_mask_amd")
     for dirpath, _, files in os.walk(pkg):

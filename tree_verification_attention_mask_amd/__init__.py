@@ -1,6 +1,7 @@
-"""MI355X (gfx950) tree-verification attention: mask build, verify attention, greedy accept.
+"""MI355X (gfx950) tree-verification attention: mask build, verify attention, greedy accept,
+and the D-cut verification budget that packs chain drafts ahead of them.
 
-The three calls are thin wrappers over the C ABI of ``lib/libtreeverify.so``
+The calls are thin wrappers over the C ABI of ``lib/libtreeverify.so``
 (``include/treeverify.h``); build it with
 ``python -m tree_verification_attention_mask_amd.build``.
 """
@@ -8,6 +9,7 @@ from .binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     TVError,
+    dcut_select,
     load_library,
     mask_struct,
     tree_accept,

@@ -24,7 +24,8 @@ MAX_ACCEPT_NODES = 8192
 
 # every symbol the header declares
 EXPORTS = ("tv_tree_mask_build", "tv_tree_verify_attn_workspace_size", "tv_tree_verify_attn",
-           "tv_tree_accept", "tv_status_string")
+           "tv_tree_accept", "tv_dcut_select", "tv_status_string")
+MAX_DCUT_DRAFT_POSITIONS = 32768
 
 
 class TVError(RuntimeError):
@@ -61,6 +62,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tv_tree_verify_attn.restype = ctypes.c_int
     lib.tv_tree_accept.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P]
     lib.tv_tree_accept.restype = ctypes.c_int
+    lib.tv_dcut_select.argtypes = [P, P, I, I, I, P, P, P, P, P]
+    lib.tv_dcut_select.restype = ctypes.c_int
     lib.tv_status_string.argtypes = [ctypes.c_int]
     lib.tv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -196,3 +199,27 @@ def tree_accept(parent: torch.Tensor, draft_tok: torch.Tensor, target_tok: torch
                             _ptr(o["path"]), _ptr(o["bonus"]), _stream(stream))
     _check("tv_tree_accept", st)
     return o["accept_len"], o["path"], o["bonus"]
+
+
+def dcut_select(conf: torch.Tensor, tokens: torch.Tensor, budget: int, out: dict | None = None,
+                stream=None):
+    """D-cut budget (``tv_dcut_select``): ``conf`` fp32 [B, D], ``tokens`` int32 [B, D+1].
+
+    Returns (n_keep [B], cu_nodes [B+1], parent [budget], packed_tokens [budget]).
+    """
+    lib = load_library()
+    assert conf.dtype == torch.float32 and conf.is_contiguous() and conf.dim() == 2
+    batch, d = conf.shape
+    assert tokens.dtype == torch.int32 and tokens.is_contiguous()
+    assert tuple(tokens.shape) == (batch, d + 1)
+    dev = conf.device
+    o = dict(out or {})
+    o.setdefault("n_keep", torch.empty(batch, dtype=torch.int32, device=dev))
+    o.setdefault("cu_nodes", torch.empty(batch + 1, dtype=torch.int32, device=dev))
+    o.setdefault("parent", torch.empty(max(int(budget), 1), dtype=torch.int32, device=dev))
+    o.setdefault("packed_tokens", torch.empty(max(int(budget), 1), dtype=torch.int32, device=dev))
+    st = lib.tv_dcut_select(_ptr(conf), _ptr(tokens), batch, d, int(budget), _ptr(o["n_keep"]),
+                            _ptr(o["cu_nodes"]), _ptr(o["parent"]), _ptr(o["packed_tokens"]),
+                            _stream(stream))
+    _check("tv_dcut_select", st)
+    return o["n_keep"], o["cu_nodes"], o["parent"][:budget], o["packed_tokens"][:budget]

@@ -132,3 +132,16 @@ extern "C" tv_status_t tv_tree_accept(const int32_t* parent, const int32_t* draf
   return launched(launch_accept(parent, draft_tok, target_tok, cu_nodes, batch, total_nodes,
                                 max_nodes, max_depth, accept_len, path, bonus_tok, stream));
 }
+
+extern "C" tv_status_t tv_dcut_select(const float* conf, const int32_t* tokens, int32_t batch,
+                                      int32_t draft_len, int32_t budget, int32_t* n_keep,
+                                      int32_t* cu_nodes, int32_t* parent, int32_t* packed_tokens,
+                                      hipStream_t stream) {
+  if (!conf || !tokens || !n_keep || !cu_nodes || !parent || !packed_tokens)
+    return TV_ERR_INVALID_ARGUMENT;
+  if (batch < 1 || draft_len < 1) return TV_ERR_INVALID_ARGUMENT;
+  if ((int64_t)batch * draft_len > TV_MAX_DCUT_DRAFT_POSITIONS) return TV_ERR_UNSUPPORTED;
+  if (budget < batch || budget > batch * (draft_len + 1)) return TV_ERR_INVALID_ARGUMENT;
+  return launched(launch_dcut_select(conf, tokens, batch, draft_len, budget, n_keep, cu_nodes,
+                                     parent, packed_tokens, stream));
+}

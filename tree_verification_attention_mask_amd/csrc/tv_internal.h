@@ -71,6 +71,11 @@ hipError_t launch_accept(const int32_t* parent, const int32_t* draft_tok, const 
                          int32_t max_nodes, int32_t max_depth, int32_t* accept_len, int32_t* path,
                          int32_t* bonus_tok, hipStream_t stream);
 
+hipError_t launch_dcut_select(const float* conf, const int32_t* tokens, int32_t batch,
+                              int32_t draft_len, int32_t budget, int32_t* n_keep,
+                              int32_t* cu_nodes, int32_t* parent, int32_t* packed_tokens,
+                              hipStream_t stream);
+
 struct AttnArgs {
   const void* q;
   const void* k_cache;
