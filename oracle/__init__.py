@@ -1,4 +1,5 @@
-"""CPU oracle for tree-verification attention -- TEST INFRASTRUCTURE.
+"""CPU oracle for tree-verification attention (and the D-cut and E2E-TV
+steps next to it) -- TEST INFRASTRUCTURE.
 
 Only the test suite, the smoke check in ``__graft_entry__`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  The product path
@@ -12,4 +13,5 @@ from .oracle import (  # noqa: F401
     tree_attn,
     accept,
     dcut_select,
+    e2e_tv_stats,
 )

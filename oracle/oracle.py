@@ -183,3 +183,40 @@ def dcut_select(conf, tokens, budget: int):
                            _p(par), _p(ptok)) != 0:
         raise ValueError("budget must lie in [batch, batch * (draft_len + 1)]")
     return n_keep, cu, par[:budget], ptok[:budget]
+
+
+def e2e_tv_stats(target_logits, draft_logits, cu_branches, temperature: float = 1.0):
+    """SpecOPD E2E-TV statistics, in float64 with numpy (no C needed).
+
+    SpecOPD §02 stage 4 and §03.2: the chance that exact rejection sampling
+    accepts the drafted token at a node is the overlap of the target's and
+    the draft's next-token distributions, alpha = sum_v min(p_v, q_v)
+    = 1 - TV(p, q); a branch's tokens are accepted consecutively, so the
+    chance of accepting its first k tokens is the product of their alphas,
+    and the expected run of accepted tokens is the sum of those products.
+
+    ``target_logits``, ``draft_logits``: [N, V] (any float dtype; bf16 tensors
+    are upcast exactly); p = softmax(target / T), q = softmax(draft / T).
+    ``cu_branches`` [B+1]: branch b is the chain of nodes [cu[b], cu[b+1]).
+    Returns (alpha [N], prefix_prob [N], expected_len [B]), float64.
+    """
+    t = _np(target_logits, np.float64) / float(temperature)
+    d = _np(draft_logits, np.float64) / float(temperature)
+    cu = _np(cu_branches, np.int64)
+    n = t.shape[0]
+    alpha = np.zeros(n, np.float64)
+    for i in range(n):
+        p = np.exp(t[i] - t[i].max())
+        p /= p.sum()
+        q = np.exp(d[i] - d[i].max())
+        q /= q.sum()
+        alpha[i] = np.minimum(p, q).sum()
+    prefix = np.zeros(n, np.float64)
+    expected = np.zeros(len(cu) - 1, np.float64)
+    for b in range(len(cu) - 1):
+        run = 1.0
+        for i in range(int(cu[b]), int(cu[b + 1])):
+            run *= alpha[i]
+            prefix[i] = run
+            expected[b] += run
+    return alpha, prefix, expected

@@ -50,3 +50,49 @@ def test_planted_oracle_mistake_is_caught(name, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, "pins did not catch mutant %s:\n%s" % (name, r.stdout[-2000:])
+
+
+# Mistakes planted in a copy of the oracle's Python front end (the E2E-TV
+# statistics are written there, in numpy); the copy is imported as `oracle`
+# before the pins run.
+PY_SRC = os.path.join(ROOT, "oracle", "oracle.py")
+PY_MUTANTS = {
+    "e2e_max_instead_of_min": ("alpha[i] = np.minimum(p, q).sum()", "alpha[i] = np.maximum(p, q).sum() - 1.0"),
+    "e2e_no_temperature": ("d = _np(draft_logits, np.float64) / float(temperature)",
+                           "d = _np(draft_logits, np.float64)"),
+    "e2e_prefix_not_reset": ("        run = 1.0\n", ""),
+    "e2e_expected_counts_root": ("            expected[b] += run", "            expected[b] += run + (i == int(cu[b]))"),
+}
+
+
+def _run_pins_with_python_oracle(tmp_path, old=None, new=None):
+    """Run the E2E-TV pins against a copy of the oracle package (optionally
+    mutated); returns pytest's exit code (0 all passed, 1 some failed)."""
+    import shutil
+    pkg = tmp_path / "oracle"
+    shutil.copytree(os.path.join(ROOT, "oracle"), pkg,
+                    ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    if old is not None:
+        src = (pkg / "oracle.py").read_text()
+        assert src.count(old) >= 1, "mutation anchor not found"
+        (pkg / "oracle.py").write_text(src.replace(old, new))
+    code = ("import sys, importlib.util\n"
+            "spec = importlib.util.spec_from_file_location('oracle', %r, submodule_search_locations=[%r])\n"
+            "m = importlib.util.module_from_spec(spec); sys.modules['oracle'] = m; spec.loader.exec_module(m)\n"
+            "import pytest\n"
+            "sys.exit(pytest.main(['-x', '-q', '-p', 'no:cacheprovider', '-k', 'e2e', %r]))\n"
+            % (str(pkg / "__init__.py"), str(pkg), os.path.join(ROOT, "tests", "test_oracle_pins.py")))
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       timeout=300)
+    return r.returncode, r.stdout
+
+
+def test_python_oracle_copy_passes_unmutated(tmp_path):
+    rc, out = _run_pins_with_python_oracle(tmp_path)
+    assert rc == 0, out[-2000:]
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_planted_python_oracle_mistake_is_caught(name, tmp_path):
+    rc, out = _run_pins_with_python_oracle(tmp_path, *PY_MUTANTS[name])
+    assert rc == 1, "pins did not catch mutant %s (exit %d):\n%s" % (name, rc, out[-2000:])

@@ -479,3 +479,63 @@ def test_dcut_packs_prefixes_in_request_order(oracle_lib):
         seg = slice(cu[b], cu[b + 1])
         assert tok[seg].tolist() == tokens[b, :n[b]].tolist()
         assert par[seg].tolist() == list(range(-1, n[b] - 1))
+
+
+# ---------------------------------------------------------------------------
+# SpecOPD E2E-TV statistics (SpecOPD §02 stage 4, §03.2): alpha = overlap of
+# the target and draft next-token distributions = 1 - TV; prefix products
+# along a branch; expected run of accepted tokens = their sum
+
+def test_e2e_alpha_is_one_minus_total_variation(oracle_lib):
+    from scipy.special import softmax
+    rng = np.random.default_rng(11)
+    t = rng.normal(0, 2, size=(6, 300))
+    d = t + rng.normal(0, 1, size=(6, 300))
+    alpha = oracle.e2e_tv_stats(t, d, [0, 6])[0]
+    tv_dist = 0.5 * np.abs(softmax(t, axis=1) - softmax(d, axis=1)).sum(axis=1)
+    np.testing.assert_allclose(alpha, 1.0 - tv_dist, rtol=0, atol=1e-12)
+
+
+def test_e2e_alpha_special_cases(oracle_lib):
+    rng = np.random.default_rng(12)
+    t = rng.normal(0, 3, size=(3, 64))
+    # identical distributions (also after a constant shift of the logits): 1
+    a = oracle.e2e_tv_stats(t, t + 5.0, [0, 3])[0]
+    np.testing.assert_allclose(a, 1.0, atol=1e-12)
+    # disjoint supports: 0
+    big = np.full((1, 8), -1e4)
+    t1, d1 = big.copy(), big.copy()
+    t1[0, 0] = 0.0
+    d1[0, 1] = 0.0
+    assert oracle.e2e_tv_stats(t1, d1, [0, 1])[0][0] < 1e-12
+    # two tokens: p = (a, 1-a), q = (b, 1-b) -> 1 - |a - b|
+    for pa, qb in [(0.3, 0.8), (0.5, 0.5), (0.99, 0.01)]:
+        t2 = np.log([[pa, 1 - pa]])
+        d2 = np.log([[qb, 1 - qb]])
+        got = oracle.e2e_tv_stats(t2, d2, [0, 1])[0][0]
+        assert abs(got - (1 - abs(pa - qb))) < 1e-12
+
+
+def test_e2e_temperature_scales_the_logits(oracle_lib):
+    rng = np.random.default_rng(13)
+    t = rng.normal(0, 2, size=(4, 100))
+    d = rng.normal(0, 2, size=(4, 100))
+    a_t = oracle.e2e_tv_stats(t, d, [0, 4], temperature=2.5)[0]
+    a_1 = oracle.e2e_tv_stats(t / 2.5, d / 2.5, [0, 4], temperature=1.0)[0]
+    np.testing.assert_allclose(a_t, a_1, atol=1e-12)
+    hot = oracle.e2e_tv_stats(t, d, [0, 4], temperature=1e6)[0]   # both near uniform
+    assert (hot > 1 - 1e-4).all()
+
+
+@pytest.mark.parametrize("w", [1, 4, 16])
+def test_e2e_chain_of_equal_alphas_is_a_geometric_series(oracle_lib, w):
+    t2 = np.log([[0.3, 0.7]] * w)
+    d2 = np.log([[0.6, 0.4]] * w)                 # alpha = 1 - 0.3 = 0.7 at every node
+    alpha, prefix, expected = oracle.e2e_tv_stats(t2, d2, [0, w])
+    a = 0.7
+    np.testing.assert_allclose(prefix, [a ** k for k in range(1, w + 1)], atol=1e-12)
+    assert abs(expected[0] - a * (1 - a ** w) / (1 - a)) < 1e-12
+    # branches are independent: splitting the same nodes into two branches
+    if w > 1:
+        _, p2, e2 = oracle.e2e_tv_stats(t2, d2, [0, 1, w])
+        assert abs(e2[0] - a) < 1e-12 and abs(p2[1] - a) < 1e-12
