@@ -295,6 +295,24 @@ def main():
         next_rows["dcut_select_us"] = time_graph(g_dcut, RS)
         next_rows["dcut_select_shape"] = "batch %d, draft_len %d, budget %d" % (
             conf_d.shape[0], conf_d.shape[1], w.meta["budget"])
+    # SpecOPD E2E-TV statistics over the branch nodes (needs both models'
+    # logits: seeded synthetic ones, target ~ N(0, 3^2), draft = target + N(0, 1))
+    if "anchors" in (w.meta or {}):
+        nb_nodes = w.total_nodes - int(w.meta["trunk"])
+        vocab = W.QWEN3_VOCAB
+        gen = torch.Generator(device=dev).manual_seed(args.config)
+        tl = (torch.randn((nb_nodes, vocab), generator=gen, device=dev) * 3.0).to(torch.bfloat16)
+        dl = (tl.float() + torch.randn((nb_nodes, vocab), generator=gen, device=dev)).to(torch.bfloat16)
+        width = nb_nodes // len(w.meta["anchors"])
+        cu_b = torch.arange(0, nb_nodes + 1, width, dtype=torch.int32, device=dev)
+        tv.e2e_tv_stats(tl, dl, cu_b)
+        g_tv = capture(lambda: [tv.e2e_tv_stats(tl, dl, cu_b) for _ in range(8)])
+        us_tv = time_graph(g_tv, 8)
+        tv_bytes = 2 * tl.numel() * tl.element_size()
+        next_rows["e2e_tv_stats_us"] = us_tv
+        next_rows["e2e_tv_stats_shape"] = "%d branch nodes x %d vocab, bf16 logits" % (nb_nodes, vocab)
+        next_rows["e2e_tv_stats_gbs"] = tv_bytes / (us_tv * 1e-6) / 1e9
+        next_rows["e2e_tv_stats_hbm_frac"] = next_rows["e2e_tv_stats_gbs"] / HBM_PEAK_GBS
     achieved_gbs = alg_bytes / (us_attn * 1e-6) / 1e9
     achieved_tflops = alg_flops / (us_attn * 1e-6) / 1e12
     plan_splits = (need > 0)

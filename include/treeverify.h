@@ -9,6 +9,9 @@
  * and, ahead of them for batches of chain drafts,
  *   0. tv_dcut_select      D-cut verification budget: rank the batch's draft
  *                          positions and pack each request's kept prefix
+ * and, after the verification pass when the caller has both models' logits,
+ *   4. tv_e2e_tv_stats     SpecOPD E2E-TV statistics: per-node acceptance
+ *                          probability 1 - TV(p, q), per-branch prefix products
  *
  * Sources (four web pages on candidate-tree speculative decoding):
  *   Graft      arXiv:2605.20104 -- 163.com article "浙江大学、阿里巴巴联手破解AI推理瓶颈"
@@ -247,6 +250,33 @@ tv_status_t tv_tree_accept(const int32_t* parent, const int32_t* draft_tok,
 tv_status_t tv_dcut_select(const float* conf, const int32_t* tokens, int32_t batch,
                            int32_t draft_len, int32_t budget, int32_t* n_keep, int32_t* cu_nodes,
                            int32_t* parent, int32_t* packed_tokens, hipStream_t stream);
+
+/*
+ * tv_e2e_tv_stats -- SpecOPD E2E-TV statistics of a set of branches.
+ *
+ * SpecOPD §02 stage 4 and §03.2: with exact rejection sampling the drafted
+ * token at a node is accepted with probability alpha = sum_v min(p_v, q_v)
+ * = 1 - TV(p, q), where p and q are the target's and the draft's next-token
+ * distributions at that node; a branch is accepted token by token, so the
+ * chance of accepting its first k tokens is the product of their alphas and
+ * the expected run of accepted tokens is the sum of those products.
+ *
+ *   target_logits, draft_logits  [num_nodes][vocab], dtype TV_BF16 or TV_F32;
+ *                p = softmax(target / T), q = softmax(draft / T); every row needs
+ *                a finite maximum
+ *   temperature  (host) T > 0 and finite
+ *   cu_branches  [num_branches + 1]: branch b is the chain of nodes [cu[b], cu[b+1])
+ *                in acceptance order (clamped into [0, num_nodes])
+ *   alpha        out [num_nodes] fp32
+ *   prefix_prob  out [num_nodes] fp32: product of alpha over the branch up to the node
+ *   expected_len out [num_branches] fp32: sum of the branch's prefix products
+ * num_branches may be 0 (then cu_branches, prefix_prob, expected_len may be NULL
+ * and only alpha is computed). One workgroup per node streams its two rows twice.
+ */
+tv_status_t tv_e2e_tv_stats(const void* target_logits, const void* draft_logits, int32_t dtype,
+                            int32_t num_nodes, int32_t vocab, float temperature,
+                            const int32_t* cu_branches, int32_t num_branches, float* alpha,
+                            float* prefix_prob, float* expected_len, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* tv_status_string(tv_status_t status);

@@ -100,6 +100,18 @@ def test_dcut_argument_checks():
     assert ds(FAKE, FAKE, 4097, 8, 5000, FAKE, FAKE, FAKE, FAKE, None) == 2  # > 32768 positions
 
 
+def test_e2e_tv_argument_checks():
+    lib = tv.load_library()
+    f = lib.tv_e2e_tv_stats
+    c = ctypes.c_float
+    assert f(None, FAKE, 1, 4, 100, c(1.0), FAKE, 1, FAKE, FAKE, FAKE, None) == 1
+    assert f(FAKE, FAKE, 1, 0, 100, c(1.0), FAKE, 1, FAKE, FAKE, FAKE, None) == 1
+    assert f(FAKE, FAKE, 1, 4, 0, c(1.0), FAKE, 1, FAKE, FAKE, FAKE, None) == 1
+    assert f(FAKE, FAKE, 5, 4, 100, c(1.0), FAKE, 1, FAKE, FAKE, FAKE, None) == 1   # dtype
+    assert f(FAKE, FAKE, 1, 4, 100, c(0.0), FAKE, 1, FAKE, FAKE, FAKE, None) == 1   # T
+    assert f(FAKE, FAKE, 1, 4, 100, c(1.0), None, 1, FAKE, FAKE, FAKE, None) == 1   # branches
+
+
 def test_product_path_never_touches_the_oracle():
     pkg = os.path.join(ROOT, "tree_verification_attention_mask_amd")
     for dirpath, _, files in os.walk(pkg):

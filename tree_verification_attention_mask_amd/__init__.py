@@ -1,5 +1,6 @@
 """MI355X (gfx950) tree-verification attention: mask build, verify attention, greedy accept,
-and the D-cut verification budget that packs chain drafts ahead of them.
+the D-cut verification budget that packs chain drafts ahead of them, and SpecOPD's
+E2E-TV statistics after them.
 
 The calls are thin wrappers over the C ABI of ``lib/libtreeverify.so``
 (``include/treeverify.h``); build it with
@@ -10,6 +11,7 @@ from .binding import (  # noqa: F401
     LIB_PATH,
     TVError,
     dcut_select,
+    e2e_tv_stats,
     load_library,
     mask_struct,
     tree_accept,

@@ -24,7 +24,7 @@ MAX_ACCEPT_NODES = 8192
 
 # every symbol the header declares
 EXPORTS = ("tv_tree_mask_build", "tv_tree_verify_attn_workspace_size", "tv_tree_verify_attn",
-           "tv_tree_accept", "tv_dcut_select", "tv_status_string")
+           "tv_tree_accept", "tv_dcut_select", "tv_e2e_tv_stats", "tv_status_string")
 MAX_DCUT_DRAFT_POSITIONS = 32768
 
 
@@ -64,6 +64,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tv_tree_accept.restype = ctypes.c_int
     lib.tv_dcut_select.argtypes = [P, P, I, I, I, P, P, P, P, P]
     lib.tv_dcut_select.restype = ctypes.c_int
+    lib.tv_e2e_tv_stats.argtypes = [P, P, I, I, I, ctypes.c_float, P, I, P, P, P, P]
+    lib.tv_e2e_tv_stats.restype = ctypes.c_int
     lib.tv_status_string.argtypes = [ctypes.c_int]
     lib.tv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -223,3 +225,28 @@ def dcut_select(conf: torch.Tensor, tokens: torch.Tensor, budget: int, out: dict
                             _stream(stream))
     _check("tv_dcut_select", st)
     return o["n_keep"], o["cu_nodes"], o["parent"][:budget], o["packed_tokens"][:budget]
+
+
+def e2e_tv_stats(target_logits: torch.Tensor, draft_logits: torch.Tensor,
+                 cu_branches: torch.Tensor | None, temperature: float = 1.0, stream=None):
+    """SpecOPD E2E-TV statistics (``tv_e2e_tv_stats``): logits [N, V] (bf16 or fp32).
+
+    Returns (alpha [N], prefix_prob [N] or None, expected_len [B] or None), fp32.
+    """
+    lib = load_library()
+    assert target_logits.shape == draft_logits.shape and target_logits.dim() == 2
+    assert target_logits.dtype == draft_logits.dtype
+    assert target_logits.is_contiguous() and draft_logits.is_contiguous()
+    n, v = target_logits.shape
+    dt = TV_F32 if target_logits.dtype == torch.float32 else TV_BF16
+    dev = target_logits.device
+    alpha = torch.empty(n, dtype=torch.float32, device=dev)
+    nb = 0 if cu_branches is None else cu_branches.numel() - 1
+    prefix = torch.empty(n, dtype=torch.float32, device=dev) if nb else None
+    expected = torch.empty(max(nb, 1), dtype=torch.float32, device=dev) if nb else None
+    cu = _dev_i32(cu_branches, dev) if nb else None
+    st = lib.tv_e2e_tv_stats(_ptr(target_logits), _ptr(draft_logits), dt, n, v,
+                             float(temperature), _ptr(cu), nb, _ptr(alpha), _ptr(prefix),
+                             _ptr(expected), _stream(stream))
+    _check("tv_e2e_tv_stats", st)
+    return alpha, prefix, expected

@@ -145,3 +145,19 @@ extern "C" tv_status_t tv_dcut_select(const float* conf, const int32_t* tokens, 
   return launched(launch_dcut_select(conf, tokens, batch, draft_len, budget, n_keep, cu_nodes,
                                      parent, packed_tokens, stream));
 }
+
+extern "C" tv_status_t tv_e2e_tv_stats(const void* target_logits, const void* draft_logits,
+                                       int32_t dtype, int32_t num_nodes, int32_t vocab,
+                                       float temperature, const int32_t* cu_branches,
+                                       int32_t num_branches, float* alpha, float* prefix_prob,
+                                       float* expected_len, hipStream_t stream) {
+  if (!target_logits || !draft_logits || !alpha) return TV_ERR_INVALID_ARGUMENT;
+  if (num_nodes < 1 || vocab < 1 || num_branches < 0) return TV_ERR_INVALID_ARGUMENT;
+  if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_INVALID_ARGUMENT;
+  if (!(temperature > 0.f) || !(temperature < 3.0e38f)) return TV_ERR_INVALID_ARGUMENT;
+  if (num_branches > 0 && (!cu_branches || !prefix_prob || !expected_len))
+    return TV_ERR_INVALID_ARGUMENT;
+  return launched(launch_e2e_tv(target_logits, draft_logits, dtype, num_nodes, vocab, temperature,
+                                cu_branches, num_branches, alpha, prefix_prob, expected_len,
+                                stream));
+}

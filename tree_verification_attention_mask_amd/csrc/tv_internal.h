@@ -76,6 +76,11 @@ hipError_t launch_dcut_select(const float* conf, const int32_t* tokens, int32_t 
                               int32_t* cu_nodes, int32_t* parent, int32_t* packed_tokens,
                               hipStream_t stream);
 
+hipError_t launch_e2e_tv(const void* target_logits, const void* draft_logits, int32_t dtype,
+                         int32_t num_nodes, int32_t vocab, float temperature,
+                         const int32_t* cu_branches, int32_t num_branches, float* alpha,
+                         float* prefix_prob, float* expected_len, hipStream_t stream);
+
 struct AttnArgs {
   const void* q;
   const void* k_cache;
