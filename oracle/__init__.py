@@ -1,5 +1,6 @@
 """CPU oracle for tree-verification attention (and the D-cut and E2E-TV
-steps next to it) -- TEST INFRASTRUCTURE.
+steps next to it: D-cut selection, E2E-TV statistics, Graft retrieval and
+its online table update) -- TEST INFRASTRUCTURE.
 
 Only the test suite, the smoke check in ``__graft_entry__`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  The product path
@@ -14,4 +15,6 @@ from .oracle import (  # noqa: F401
     accept,
     dcut_select,
     e2e_tv_stats,
+    graft_retrieve,
+    graft_update,
 )

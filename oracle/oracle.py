@@ -220,3 +220,50 @@ def e2e_tv_stats(target_logits, draft_logits, cu_branches, temperature: float = 
             prefix[i] = run
             expected[b] += run
     return alpha, prefix, expected
+
+
+def graft_retrieve(adj, root_tokens, tmpl_parent, tmpl_rank):
+    """Graft retrieval (Graft §二, second gear): expand a template from each
+    request's current token through the adjacency table.
+
+    ``adj`` int32 [V, k]: row t = the k most likely successors of token t
+    (-1 = empty). Template node j hangs under template node tmpl_parent[j]
+    (-1 = the current token) and takes that token's tmpl_rank[j]-th
+    successor; a node whose parent has no token, or whose table entry is
+    empty or out of range, has no token (-1). Returns int32 [B, T].
+    """
+    adj = _np(adj, np.int32)
+    roots = _np(root_tokens, np.int32)
+    par = [int(x) for x in tmpl_parent]
+    rank = [int(x) for x in tmpl_rank]
+    v, k = adj.shape
+    out = np.full((len(roots), len(par)), -1, np.int32)
+    for b, root in enumerate(roots):
+        for j in range(len(par)):
+            src = int(root) if par[j] < 0 else int(out[b, par[j]])
+            if 0 <= src < v and 0 <= rank[j] < k:
+                t = int(adj[src, rank[j]])
+                out[b, j] = t if 0 <= t < v else -1
+    return out
+
+
+def graft_update(adj, target_logits, node_tokens):
+    """Graft online update (Graft §二 third gear, §五): after verification the
+    row of every verified node's token is replaced by the target's k most
+    likely next tokens at that node (larger logit first, ties to the smaller
+    token id); when several nodes carry the same token the later node's row
+    is kept. Tokens outside [0, V) update nothing; NaN logits rank as -inf.
+    Returns the new table."""
+    adj = _np(adj, np.int32).copy()
+    logits = _np(target_logits, np.float32)
+    tok = _np(node_tokens, np.int32)
+    v, k = adj.shape
+    ids = np.arange(v)
+    for i in range(len(tok)):              # in node order: a later node overwrites
+        t = int(tok[i])
+        if not (0 <= t < v):
+            continue
+        key = np.where(np.isnan(logits[i]), -np.inf, logits[i]).astype(np.float64)
+        order = np.lexsort((ids, -key))     # by logit descending, then token id
+        adj[t] = order[:k]
+    return adj

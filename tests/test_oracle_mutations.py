@@ -61,12 +61,18 @@ PY_MUTANTS = {
     "e2e_no_temperature": ("d = _np(draft_logits, np.float64) / float(temperature)",
                            "d = _np(draft_logits, np.float64)"),
     "e2e_prefix_not_reset": ("        run = 1.0\n", ""),
+    "graft_parent_is_previous_node": ("src = int(root) if par[j] < 0 else int(out[b, par[j]])",
+                                      "src = int(root) if par[j] < 0 else int(out[b, j - 1])"),
+    "graft_rank_ignored": ("t = int(adj[src, rank[j]])", "t = int(adj[src, 0])"),
+    "graft_first_writer_wins": ("    for i in range(len(tok)):              # in node order: a later node overwrites",
+                                "    for i in reversed(range(len(tok))):"),
+    "graft_ties_to_larger_id": ("order = np.lexsort((ids, -key))", "order = np.lexsort((-ids, -key))"),
     "e2e_expected_counts_root": ("            expected[b] += run", "            expected[b] += run + (i == int(cu[b]))"),
 }
 
 
 def _run_pins_with_python_oracle(tmp_path, old=None, new=None):
-    """Run the E2E-TV pins against a copy of the oracle package (optionally
+    """Run the E2E-TV and Graft pins against a copy of the oracle package (optionally
     mutated); returns pytest's exit code (0 all passed, 1 some failed)."""
     import shutil
     pkg = tmp_path / "oracle"
@@ -80,7 +86,7 @@ def _run_pins_with_python_oracle(tmp_path, old=None, new=None):
             "spec = importlib.util.spec_from_file_location('oracle', %r, submodule_search_locations=[%r])\n"
             "m = importlib.util.module_from_spec(spec); sys.modules['oracle'] = m; spec.loader.exec_module(m)\n"
             "import pytest\n"
-            "sys.exit(pytest.main(['-x', '-q', '-p', 'no:cacheprovider', '-k', 'e2e', %r]))\n"
+            "sys.exit(pytest.main(['-x', '-q', '-p', 'no:cacheprovider', '-k', 'e2e or graft', %r]))\n"
             % (str(pkg / "__init__.py"), str(pkg), os.path.join(ROOT, "tests", "test_oracle_pins.py")))
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
                        timeout=300)

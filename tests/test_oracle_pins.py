@@ -539,3 +539,89 @@ def test_e2e_chain_of_equal_alphas_is_a_geometric_series(oracle_lib, w):
     if w > 1:
         _, p2, e2 = oracle.e2e_tv_stats(t2, d2, [0, 1, w])
         assert abs(e2[0] - a) < 1e-12 and abs(p2[1] - a) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Graft retrieval and online update (Graft §二 second and third gear, §五):
+# a device table of each token's top-k successors, a template expanded from
+# the current token, rows replaced by the target's top-k after verification
+
+def _succ_table(v, k, step=1):
+    """Row t lists t+step, t+2*step, ... (mod v): successors with a closed form."""
+    return np.array([[(t + step * (r + 1)) % v for r in range(k)] for t in range(v)], np.int32)
+
+
+def test_graft_retrieve_follows_ranks_along_the_template(oracle_lib):
+    v, k = 97, 4
+    adj = _succ_table(v, k)
+    # chain of depth 5 taking ranks 0, 2, 1, 3, 0, a second child of the root,
+    # and a node hanging under the chain's second node (not the node before it)
+    par = [-1, 0, 1, 2, 3, -1, 1]
+    rank = [0, 2, 1, 3, 0, 2, 1]
+    out = oracle.graft_retrieve(adj, [5, 90], par, rank)
+    for b, root in enumerate([5, 90]):
+        t, exp = root, []
+        for r in rank[:5]:
+            t = (t + r + 1) % v
+            exp.append(t)
+        exp.append((root + 3) % v)
+        exp.append((exp[1] + 2) % v)     # under node 1 (token root+4), not node 5 (root+3)
+        assert out[b].tolist() == exp
+
+
+def test_graft_retrieve_missing_entries_empty_the_subtree(oracle_lib):
+    v, k = 20, 3
+    adj = _succ_table(v, k)
+    adj[6, 1] = -1                      # token 6 lacks its second successor
+    adj[7, 0] = 99                      # out of the vocabulary
+    par, rank = [-1, 0, 1, -1, 3], [0, 0, 0, 1, 0]
+    out = oracle.graft_retrieve(adj, [5, 6, -3], par, rank)
+    # from 5: 6, then 7, then adj[7][0] = 99 (out of range) -> -1; 5's 2nd is 7 -> -1 below
+    assert out[0].tolist() == [6, 7, -1, 7, -1]
+    # from 6: 7, -1, -1; 6's 2nd successor is missing, so its child is too
+    assert out[1].tolist() == [7, -1, -1, -1, -1]
+    assert out[2].tolist() == [-1] * 5              # no current token
+
+
+def test_graft_update_takes_the_targets_top_k(oracle_lib):
+    rng = np.random.default_rng(21)
+    v, k = 1000, 8
+    adj = _succ_table(v, k)
+    centre = [100, 500, 999]
+    u = np.arange(v)
+    # logits falling with the distance from a centre (plus a tiny tie-breaking
+    # slope): the top-k are the k tokens nearest the centre, nearest first
+    logits = np.stack([-np.abs(u - c) - 1e-3 * u for c in centre]).astype(np.float32)
+    new = oracle.graft_update(adj, logits, [3, 4, 5])
+    for row, c in zip((3, 4, 5), centre):
+        near = sorted(u, key=lambda x: (abs(x - c), x))[:k]
+        assert new[row].tolist() == near
+    untouched = np.setdiff1d(u, [3, 4, 5])
+    np.testing.assert_array_equal(new[untouched], adj[untouched])
+    flat = oracle.graft_update(adj, np.zeros((1, v), np.float32), [7])
+    assert flat[7].tolist() == list(range(k))       # all equal: smallest ids
+
+
+def test_graft_update_later_node_wins_and_nan_ranks_last(oracle_lib):
+    v, k = 50, 3
+    adj = _succ_table(v, k)
+    lg = np.full((3, v), -5.0, np.float32)
+    lg[0, 10] = 1.0
+    lg[1, 20] = 1.0
+    lg[2, [30, 31]] = np.nan
+    lg[2, 40] = 2.0
+    new = oracle.graft_update(adj, lg, [9, 9, 11])
+    assert new[9].tolist() == [20, 0, 1]            # node 1 (later) wins row 9
+    assert new[11].tolist() == [40, 0, 1]           # NaNs never outrank finite logits
+    assert oracle.graft_update(adj, lg, [-1, 50, 1000]).tolist() == adj.tolist()
+
+
+def test_graft_update_then_retrieve_follows_the_new_rows(oracle_lib):
+    v, k = 64, 2
+    adj = np.full((v, k), -1, np.int32)
+    lg = np.full((3, v), -1.0, np.float32)
+    lg[0, 11] = 1.0        # after token 10 the target expects 11, then 12 ...
+    lg[1, 12] = 1.0
+    lg[2, 13] = 1.0
+    adj = oracle.graft_update(adj, lg, [10, 11, 12])
+    assert oracle.graft_retrieve(adj, [10], [-1, 0, 1], [0, 0, 0])[0].tolist() == [11, 12, 13]
