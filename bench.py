@@ -313,6 +313,40 @@ def main():
         next_rows["e2e_tv_stats_shape"] = "%d branch nodes x %d vocab, bf16 logits" % (nb_nodes, vocab)
         next_rows["e2e_tv_stats_gbs"] = tv_bytes / (us_tv * 1e-6) / 1e9
         next_rows["e2e_tv_stats_hbm_frac"] = next_rows["e2e_tv_stats_gbs"] / HBM_PEAK_GBS
+    # Graft's retrieval table for the Graft-shaped tree: the online update from
+    # the target's logits at the 60 verified nodes (seeded synthetic logits,
+    # N(0, 3^2)) and the 20-slot retrieval template under the graft point
+    if w.name == W.CONFIG_NAMES[2]:
+        vocab, k_adj = W.QWEN3_VOCAB, 8
+        gen = torch.Generator(device=dev).manual_seed(args.config)
+        adj = torch.randint(0, vocab, (vocab, k_adj), generator=gen, device=dev, dtype=torch.int32)
+        lg = (torch.randn((w.total_nodes, vocab), generator=gen, device=dev) * 3.0).to(torch.bfloat16)
+        node_tok = torch.randint(0, vocab, (w.total_nodes,), generator=gen, device=dev,
+                                 dtype=torch.int32)
+        par_t, rank_t, seen, kids = [], [], {W.GRAFT_TREE_PARENT[40]: -1}, {}
+        for j in range(40, 60):
+            seen[j] = j - 40
+            pp = seen[W.GRAFT_TREE_PARENT[j]]
+            kids[pp] = kids.get(pp, 0) + 1
+            par_t.append(pp)
+            rank_t.append(kids[pp] - 1)
+        roots = node_tok[:1].clone()
+        ret_out = torch.empty((1, len(par_t)), dtype=torch.int32, device=dev)
+        ws_up = torch.empty(max(1, tv.graft_update_workspace_size(w.total_nodes, vocab, k_adj)),
+                            dtype=torch.uint8, device=dev)
+        tv.graft_update(adj, lg, node_tok, workspace=ws_up)
+        tv.graft_retrieve(adj, roots, par_t, rank_t, out=ret_out)
+        g_up = capture(lambda: [tv.graft_update(adj, lg, node_tok, workspace=ws_up)
+                                for _ in range(RS)])
+        g_ret = capture(lambda: [tv.graft_retrieve(adj, roots, par_t, rank_t, out=ret_out)
+                                 for _ in range(RS)])
+        us_up = time_graph(g_up, RS)
+        next_rows["graft_update_us"] = us_up
+        next_rows["graft_update_gbs"] = 2 * lg.numel() / (us_up * 1e-6) / 1e9
+        next_rows["graft_update_shape"] = "%d verified nodes x %d vocab bf16 logits, k %d" % (
+            w.total_nodes, vocab, k_adj)
+        next_rows["graft_retrieve_us"] = time_graph(g_ret, RS)
+        next_rows["graft_retrieve_shape"] = "1 request, 20-slot template (depth %d)" % 5
     achieved_gbs = alg_bytes / (us_attn * 1e-6) / 1e9
     achieved_tflops = alg_flops / (us_attn * 1e-6) / 1e12
     plan_splits = (need > 0)

@@ -12,6 +12,11 @@
  * and, after the verification pass when the caller has both models' logits,
  *   4. tv_e2e_tv_stats     SpecOPD E2E-TV statistics: per-node acceptance
  *                          probability 1 - TV(p, q), per-branch prefix products
+ *   5. tv_graft_update     Graft: refresh the successor table from the target's
+ *                          next-token logits at the verified nodes
+ * and, while building the next tree,
+ *   6. tv_graft_retrieve   Graft: fill freed slots by expanding a template from
+ *                          the current token through that table
  *
  * Sources (four web pages on candidate-tree speculative decoding):
  *   Graft      arXiv:2605.20104 -- 163.com article "浙江大学、阿里巴巴联手破解AI推理瓶颈"
@@ -277,6 +282,63 @@ tv_status_t tv_e2e_tv_stats(const void* target_logits, const void* draft_logits,
                             int32_t num_nodes, int32_t vocab, float temperature,
                             const int32_t* cu_branches, int32_t num_branches, float* alpha,
                             float* prefix_prob, float* expected_len, hipStream_t stream);
+
+/*
+ * tv_graft_retrieve -- Graft retrieval: expand a template from each request's
+ * current token through the successor table.
+ *
+ * Graft §二 (second gear): a table in GPU memory holds, per vocabulary token,
+ * its k most likely successors, ranked; the slots freed by pruning are filled
+ * by expanding a stage-specific template rooted at the current token, one row
+ * lookup per template node. The page gives the slot budgets (52 / 36 / 20)
+ * but not the template shapes: the template is the caller's.
+ *
+ *   adj          [vocab][k] int32: row t = successors of token t, best first; -1 = empty
+ *   root_tokens  [batch]: each request's current token
+ *   tmpl_parent  (host) [tmpl_nodes]: parent template node (< j), or -1 for the current token
+ *   tmpl_rank    (host) [tmpl_nodes]: which successor (0 .. k-1) the node takes
+ *   out_tokens   out [batch][tmpl_nodes]: retrieved tokens; -1 where the parent has no
+ *                token or the table entry is empty or outside [0, vocab)
+ * Limits: 1 <= k <= TV_MAX_GRAFT_K, 1 <= tmpl_nodes <= TV_MAX_GRAFT_TEMPLATE
+ * (TV_ERR_UNSUPPORTED beyond); a template that is not in topological order or
+ * has a rank outside [0, k) is TV_ERR_INVALID_ARGUMENT.
+ */
+#define TV_MAX_GRAFT_K 16
+#define TV_MAX_GRAFT_TEMPLATE 64
+tv_status_t tv_graft_retrieve(const int32_t* adj, int32_t vocab, int32_t k,
+                              const int32_t* root_tokens, int32_t batch,
+                              const int32_t* tmpl_parent, const int32_t* tmpl_rank,
+                              int32_t tmpl_nodes, int32_t* out_tokens, hipStream_t stream);
+
+/*
+ * tv_graft_update -- Graft online update of the successor table.
+ *
+ * Graft §二 (third gear) and §五: after the verification pass, the target's
+ * next-token distribution at every verified node (accepted or not) replaces
+ * the table row of that node's token with the target's k most likely next
+ * tokens. Ranking is by logit (softmax is monotone), ties to the smaller
+ * token id, NaN as -inf. When several nodes carry the same token, the later
+ * node (larger index) writes the row. Tokens outside [0, vocab) update
+ * nothing; other rows are untouched.
+ *
+ *   adj          in/out [vocab][k] int32
+ *   target_logits [num_nodes][vocab], dtype TV_BF16 or TV_F32 (16-byte aligned
+ *                rows with vocab a multiple of 8 (bf16) / 4 (fp32) take the
+ *                vector path; any other layout works, more slowly)
+ *   node_tokens  [num_nodes]: the token at each verified node
+ *   workspace    >= tv_graft_update_workspace_size(...) bytes, 256-byte aligned,
+ *                or NULL when that size is 0 (one workgroup per row); partial
+ *                top-k lists of the row shares. Contents on entry are ignored;
+ *                calls that share a workspace must not overlap in time.
+ * Limits: 1 <= k <= min(TV_MAX_GRAFT_K, vocab); vocab <= TV_MAX_GRAFT_VOCAB
+ * (TV_ERR_UNSUPPORTED beyond). A workspace below the size is TV_ERR_WORKSPACE.
+ */
+#define TV_MAX_GRAFT_VOCAB (1 << 30)
+size_t tv_graft_update_workspace_size(int32_t num_nodes, int32_t vocab, int32_t k,
+                                      int32_t dtype);
+tv_status_t tv_graft_update(int32_t* adj, int32_t vocab, int32_t k, const void* target_logits,
+                            int32_t dtype, int32_t num_nodes, const int32_t* node_tokens,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* tv_status_string(tv_status_t status);

@@ -112,6 +112,33 @@ def test_e2e_tv_argument_checks():
     assert f(FAKE, FAKE, 1, 4, 100, c(1.0), None, 1, FAKE, FAKE, FAKE, None) == 1   # branches
 
 
+def test_graft_argument_checks():
+    lib = tv.load_library()
+    I3 = ctypes.c_int32 * 3
+    par, rank = I3(-1, 0, 1), I3(0, 1, 0)
+    r = lib.tv_graft_retrieve
+    assert r(None, 10, 4, FAKE, 2, par, rank, 3, FAKE, None) == 1
+    assert r(FAKE, 10, 17, FAKE, 2, par, rank, 3, FAKE, None) == 2          # k > 16
+    assert r(FAKE, 10, 4, FAKE, 2, I3(-1, 2, 0), rank, 3, FAKE, None) == 1  # not topological
+    assert r(FAKE, 10, 1, FAKE, 2, par, rank, 3, FAKE, None) == 1          # rank 1 >= k
+    u = lib.tv_graft_update
+    assert u(FAKE, 10, 11, FAKE, 1, 4, FAKE, None, 0, None) == 1          # k > vocab
+    assert u(FAKE, 100, 17, FAKE, 1, 4, FAKE, None, 0, None) == 2
+    assert u(FAKE, 100, 8, FAKE, 3, 4, FAKE, None, 0, None) == 1          # dtype
+    assert u(FAKE, (1 << 30) + 1, 8, FAKE, 1, 4, FAKE, None, 0, None) == 2  # vocab
+    ws = lib.tv_graft_update_workspace_size
+    assert ws(4, 100, 8, 1) == 0                 # one workgroup per row
+    need = ws(60, 151936, 8, 1)                  # a row per verified node: split rows
+    assert need > 0 and need % 256 == 0
+    assert ws(60, 151936, 8, 0) > 0
+    assert ws(60, 151936, 8, 3) == 0             # bad dtype: nothing to size
+    assert ws(9, 5, 1, 1) == 0 and ws(1, 1, 1, 0) == 0   # below one 16-byte group
+    # a workspace below the size is refused before anything is launched (this
+    # shape splits rows the same way on the 16-byte and the one-value path)
+    assert u(FAKE, 151936, 8, FAKE, 1, 60, FAKE, None, 0, None) == 3
+    assert u(FAKE, 151936, 8, FAKE, 1, 60, FAKE, FAKE, need - 1, None) == 3
+
+
 def test_product_path_never_touches_the_oracle():
     pkg = os.path.join(ROOT, "tree_verification_attention_mask_amd")
     for dirpath, _, files in os.walk(pkg):

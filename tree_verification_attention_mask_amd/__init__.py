@@ -1,6 +1,7 @@
 """MI355X (gfx950) tree-verification attention: mask build, verify attention, greedy accept,
 the D-cut verification budget that packs chain drafts ahead of them, and SpecOPD's
-E2E-TV statistics after them.
+E2E-TV statistics after them, and Graft's retrieval table (template expansion and
+online update).
 
 The calls are thin wrappers over the C ABI of ``lib/libtreeverify.so``
 (``include/treeverify.h``); build it with
@@ -12,6 +13,9 @@ from .binding import (  # noqa: F401
     TVError,
     dcut_select,
     e2e_tv_stats,
+    graft_retrieve,
+    graft_update,
+    graft_update_workspace_size,
     load_library,
     mask_struct,
     tree_accept,

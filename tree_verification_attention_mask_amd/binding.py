@@ -24,7 +24,8 @@ MAX_ACCEPT_NODES = 8192
 
 # every symbol the header declares
 EXPORTS = ("tv_tree_mask_build", "tv_tree_verify_attn_workspace_size", "tv_tree_verify_attn",
-           "tv_tree_accept", "tv_dcut_select", "tv_e2e_tv_stats", "tv_status_string")
+           "tv_tree_accept", "tv_dcut_select", "tv_e2e_tv_stats", "tv_graft_retrieve",
+           "tv_graft_update_workspace_size", "tv_graft_update", "tv_status_string")
 MAX_DCUT_DRAFT_POSITIONS = 32768
 
 
@@ -66,6 +67,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tv_dcut_select.restype = ctypes.c_int
     lib.tv_e2e_tv_stats.argtypes = [P, P, I, I, I, ctypes.c_float, P, I, P, P, P, P]
     lib.tv_e2e_tv_stats.restype = ctypes.c_int
+    lib.tv_graft_retrieve.argtypes = [P, I, I, P, I, P, P, I, P, P]
+    lib.tv_graft_retrieve.restype = ctypes.c_int
+    lib.tv_graft_update_workspace_size.argtypes = [I, I, I, I]
+    lib.tv_graft_update_workspace_size.restype = S
+    lib.tv_graft_update.argtypes = [P, I, I, P, I, I, P, P, S, P]
+    lib.tv_graft_update.restype = ctypes.c_int
     lib.tv_status_string.argtypes = [ctypes.c_int]
     lib.tv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -250,3 +257,55 @@ def e2e_tv_stats(target_logits: torch.Tensor, draft_logits: torch.Tensor,
                              _ptr(expected), _stream(stream))
     _check("tv_e2e_tv_stats", st)
     return alpha, prefix, expected
+
+
+def graft_retrieve(adj: torch.Tensor, root_tokens: torch.Tensor, tmpl_parent, tmpl_rank,
+                   out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Graft retrieval (``tv_graft_retrieve``): ``adj`` int32 [V, k], template as host lists.
+
+    Returns int32 [B, T] retrieved tokens (-1 where there is none).
+    """
+    lib = load_library()
+    assert adj.dtype == torch.int32 and adj.is_contiguous() and adj.dim() == 2
+    v, k = adj.shape
+    roots = _dev_i32(root_tokens, adj.device)
+    par = (ctypes.c_int32 * len(tmpl_parent))(*[int(x) for x in tmpl_parent])
+    rank = (ctypes.c_int32 * len(tmpl_rank))(*[int(x) for x in tmpl_rank])
+    assert len(tmpl_parent) == len(tmpl_rank)
+    if out is None:
+        out = torch.empty((roots.numel(), len(tmpl_parent)), dtype=torch.int32, device=adj.device)
+    st = lib.tv_graft_retrieve(_ptr(adj), v, k, _ptr(roots), roots.numel(), par, rank,
+                               len(tmpl_parent), _ptr(out), _stream(stream))
+    _check("tv_graft_retrieve", st)
+    return out
+
+
+def graft_update_workspace_size(num_nodes: int, vocab: int, k: int, dtype=torch.bfloat16) -> int:
+    """Bytes ``tv_graft_update`` needs for these shapes (0: none)."""
+    dt = TV_F32 if dtype == torch.float32 else TV_BF16
+    return int(load_library().tv_graft_update_workspace_size(num_nodes, vocab, k, dt))
+
+
+def graft_update(adj: torch.Tensor, target_logits: torch.Tensor, node_tokens: torch.Tensor,
+                 workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Graft online update (``tv_graft_update``), in place on ``adj`` int32 [V, k].
+
+    ``workspace`` (uint8, device) is allocated here when absent or too small.
+    """
+    lib = load_library()
+    assert adj.dtype == torch.int32 and adj.is_contiguous() and adj.dim() == 2
+    v, k = adj.shape
+    assert target_logits.dim() == 2 and target_logits.shape[1] == v
+    assert target_logits.is_contiguous()
+    dt = TV_F32 if target_logits.dtype == torch.float32 else TV_BF16
+    tok = _dev_i32(node_tokens, adj.device)
+    n = tok.numel()
+    assert n == target_logits.shape[0]
+    need = int(lib.tv_graft_update_workspace_size(n, v, k, dt))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=adj.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.tv_graft_update(_ptr(adj), v, k, _ptr(target_logits), dt, n, _ptr(tok),
+                             _ptr(workspace), ws_bytes, _stream(stream))
+    _check("tv_graft_update", st)
+    return adj

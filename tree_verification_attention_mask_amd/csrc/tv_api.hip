@@ -161,3 +161,51 @@ extern "C" tv_status_t tv_e2e_tv_stats(const void* target_logits, const void* dr
                                 cu_branches, num_branches, alpha, prefix_prob, expected_len,
                                 stream));
 }
+
+extern "C" tv_status_t tv_graft_retrieve(const int32_t* adj, int32_t vocab, int32_t k,
+                                         const int32_t* root_tokens, int32_t batch,
+                                         const int32_t* tmpl_parent, const int32_t* tmpl_rank,
+                                         int32_t tmpl_nodes, int32_t* out_tokens,
+                                         hipStream_t stream) {
+  if (!adj || !root_tokens || !tmpl_parent || !tmpl_rank || !out_tokens)
+    return TV_ERR_INVALID_ARGUMENT;
+  if (vocab < 1 || k < 1 || batch < 1 || tmpl_nodes < 1) return TV_ERR_INVALID_ARGUMENT;
+  if (k > TV_MAX_GRAFT_K || tmpl_nodes > TV_MAX_GRAFT_TEMPLATE) return TV_ERR_UNSUPPORTED;
+  for (int j = 0; j < tmpl_nodes; ++j) {  // host template: topological, ranks in range
+    if (tmpl_parent[j] < -1 || tmpl_parent[j] >= j) return TV_ERR_INVALID_ARGUMENT;
+    if (tmpl_rank[j] < 0 || tmpl_rank[j] >= k) return TV_ERR_INVALID_ARGUMENT;
+  }
+  return launched(launch_graft_retrieve(adj, vocab, k, root_tokens, batch, tmpl_parent, tmpl_rank,
+                                        tmpl_nodes, out_tokens, stream));
+}
+
+extern "C" size_t tv_graft_update_workspace_size(int32_t num_nodes, int32_t vocab, int32_t k,
+                                                 int32_t dtype) {
+  if (vocab < 1 || k < 1 || num_nodes < 1 || k > vocab || k > TV_MAX_GRAFT_K) return 0;
+  if (dtype != TV_F32 && dtype != TV_BF16) return 0;
+  // the alignment of the logits picks the 16-byte or the one-value path: size
+  // for either
+  const size_t a = graft_update_workspace(num_nodes, vocab, k, dtype, false);
+  const size_t b = graft_update_workspace(num_nodes, vocab, k, dtype, true);
+  return a > b ? a : b;
+}
+
+extern "C" tv_status_t tv_graft_update(int32_t* adj, int32_t vocab, int32_t k,
+                                       const void* target_logits, int32_t dtype,
+                                       int32_t num_nodes, const int32_t* node_tokens,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+  if (!adj || !target_logits || !node_tokens) return TV_ERR_INVALID_ARGUMENT;
+  if (vocab < 1 || k < 1 || num_nodes < 1 || k > vocab) return TV_ERR_INVALID_ARGUMENT;
+  if (vocab > TV_MAX_GRAFT_VOCAB) return TV_ERR_UNSUPPORTED;
+  if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_INVALID_ARGUMENT;
+  if (k > TV_MAX_GRAFT_K) return TV_ERR_UNSUPPORTED;
+  const size_t need = graft_update_workspace(num_nodes, vocab, k, dtype,
+                                             graft_update_vec(target_logits, dtype, vocab));
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return TV_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255) return TV_ERR_INVALID_ARGUMENT;
+  }
+  return launched(launch_graft_update(adj, vocab, k, target_logits, dtype, num_nodes, node_tokens,
+                                      workspace, stream));
+}

@@ -81,6 +81,18 @@ hipError_t launch_e2e_tv(const void* target_logits, const void* draft_logits, in
                          const int32_t* cu_branches, int32_t num_branches, float* alpha,
                          float* prefix_prob, float* expected_len, hipStream_t stream);
 
+hipError_t launch_graft_retrieve(const int32_t* adj, int32_t vocab, int32_t k,
+                                 const int32_t* root_tokens, int32_t batch,
+                                 const int32_t* tmpl_parent, const int32_t* tmpl_rank,
+                                 int32_t tmpl_nodes, int32_t* out_tokens, hipStream_t stream);
+// bytes of split partial lists the update needs (0: one workgroup per row)
+size_t graft_update_workspace(int32_t num_nodes, int32_t vocab, int32_t k, int32_t dtype,
+                              bool vec);
+bool graft_update_vec(const void* logits, int32_t dtype, int32_t vocab);
+hipError_t launch_graft_update(int32_t* adj, int32_t vocab, int32_t k, const void* logits,
+                               int32_t dtype, int32_t num_nodes, const int32_t* node_tokens,
+                               void* workspace, hipStream_t stream);
+
 struct AttnArgs {
   const void* q;
   const void* k_cache;
