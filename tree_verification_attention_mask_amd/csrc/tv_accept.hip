@@ -13,7 +13,7 @@
 // same chunk is resolved by pointer jumping over the lanes (6 shuffle rounds
 // for 64 lanes). state(i) = depth(i) if i is accepted, else -1. The deepest
 // accepted node (ties: smallest index) wins a wave max-reduction.
-#include "tv_internal.h"
+#include "tv_launch.h"
 
 namespace tv {
 namespace {

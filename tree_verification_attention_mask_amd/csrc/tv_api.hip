@@ -2,7 +2,7 @@
 // kernel launches. Nothing here allocates, frees or synchronises.
 #include <algorithm>
 
-#include "tv_internal.h"
+#include "tv_launch.h"
 
 using namespace tv;
 

@@ -17,7 +17,7 @@
 //      handed out in request order (a block scan) -- the tie rule;
 //   4. cu_nodes by a second block scan, then the packed chains and tokens.
 // Threads own contiguous runs of requests, so scans keep request order.
-#include "tv_internal.h"
+#include "tv_launch.h"
 
 namespace tv {
 namespace {

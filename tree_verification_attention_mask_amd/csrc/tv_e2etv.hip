@@ -16,7 +16,7 @@
 //           exp2 per vocabulary entry. The second pass re-reads rows the
 //           first pass just brought through L2 / the last-level cache.
 // branch_kernel: one thread per branch, prefix products and their sum.
-#include "tv_internal.h"
+#include "tv_launch.h"
 
 namespace tv {
 namespace {

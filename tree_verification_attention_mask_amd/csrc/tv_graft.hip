@@ -24,7 +24,7 @@
 //   waves' lists; the merge kernel ranks the shares' lists and writes the
 //   row. A row is written only when no later node carries the same token,
 //   so every row has one writer.
-#include "tv_internal.h"
+#include "tv_launch.h"
 
 namespace tv {
 namespace {

@@ -1,5 +1,6 @@
-// tv_internal.h -- declarations shared by the library's own translation units.
-// Device helpers and launch entry points; nothing here is part of the C ABI.
+// tv_internal.h -- what the attention kernel compiles against: the mask as the
+// kernels see it, tile visibility, and the attention launch plan. Nothing here
+// is part of the C ABI; the other kernels' launchers are in tv_launch.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -59,40 +60,6 @@ __device__ __forceinline__ uint64_t tile_visibility(const MaskDev& mk, int node,
   return v;
 }
 
-// ---- launchers (each returns the launch's hipError_t) ----
-hipError_t launch_mask_bits(const int32_t* parent, const int32_t* cu_nodes, int32_t batch,
-                            int32_t total_nodes, int32_t words, uint64_t* bits, int32_t* depth,
-                            int32_t* err, hipStream_t stream);
-hipError_t launch_mask_anchor(const int32_t* parent, const int32_t* cu_nodes, int32_t batch,
-                              int32_t total_nodes, int32_t* anchor_pos, int32_t* branch_depth,
-                              int32_t* depth, int32_t* err, hipStream_t stream);
-hipError_t launch_accept(const int32_t* parent, const int32_t* draft_tok, const int32_t* target_tok,
-                         const int32_t* cu_nodes, int32_t batch, int32_t total_nodes,
-                         int32_t max_nodes, int32_t max_depth, int32_t* accept_len, int32_t* path,
-                         int32_t* bonus_tok, hipStream_t stream);
-
-hipError_t launch_dcut_select(const float* conf, const int32_t* tokens, int32_t batch,
-                              int32_t draft_len, int32_t budget, int32_t* n_keep,
-                              int32_t* cu_nodes, int32_t* parent, int32_t* packed_tokens,
-                              hipStream_t stream);
-
-hipError_t launch_e2e_tv(const void* target_logits, const void* draft_logits, int32_t dtype,
-                         int32_t num_nodes, int32_t vocab, float temperature,
-                         const int32_t* cu_branches, int32_t num_branches, float* alpha,
-                         float* prefix_prob, float* expected_len, hipStream_t stream);
-
-hipError_t launch_graft_retrieve(const int32_t* adj, int32_t vocab, int32_t k,
-                                 const int32_t* root_tokens, int32_t batch,
-                                 const int32_t* tmpl_parent, const int32_t* tmpl_rank,
-                                 int32_t tmpl_nodes, int32_t* out_tokens, hipStream_t stream);
-// bytes of split partial lists the update needs (0: one workgroup per row)
-size_t graft_update_workspace(int32_t num_nodes, int32_t vocab, int32_t k, int32_t dtype,
-                              bool vec);
-bool graft_update_vec(const void* logits, int32_t dtype, int32_t vocab);
-hipError_t launch_graft_update(int32_t* adj, int32_t vocab, int32_t k, const void* logits,
-                               int32_t dtype, int32_t num_nodes, const int32_t* node_tokens,
-                               void* workspace, hipStream_t stream);
-
 struct AttnArgs {
   const void* q;
   const void* k_cache;
@@ -123,6 +90,7 @@ struct AttnPlan {
 };
 AttnPlan plan_attn(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_prefix_len,
                    int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype);
+// returns the launch's hipError_t
 hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream);
 
 }  // namespace tv

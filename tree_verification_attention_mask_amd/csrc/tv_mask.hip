@@ -11,7 +11,7 @@
 // at most 64 nodes use one wavefront and lane shuffles instead. ANCHOR
 // form: the trunk length is a block-wide min, and each branch node finds its
 // branch start with a block-wide running-max scan.
-#include "tv_internal.h"
+#include "tv_launch.h"
 
 namespace tv {
 namespace {
