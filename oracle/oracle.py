@@ -267,3 +267,100 @@ def graft_update(adj, target_logits, node_tokens):
         order = np.lexsort((ids, -key))     # by logit descending, then token id
         adj[t] = order[:k]
     return adj
+
+
+def _dist(logits_row, temperature):
+    """softmax(logits / T) in float64, NaN logits as -inf."""
+    y = np.where(np.isnan(logits_row), -np.inf, logits_row).astype(np.float64) / temperature
+    e = np.exp(y - y.max())
+    return e / e.sum()
+
+
+def accept_sampled(parent, draft_tok, cu_nodes, target_logits, draft_logits, temperature,
+                   u_accept, u_bonus, max_depth: int):
+    """Stochastic tree verification, in float64 with numpy (no C needed).
+
+    The pages verify at temperature 1 (BlockPilot §五, D-cut §4) and fix the
+    one-token rule (SpecOPD §03.2: exact rejection sampling accepts a drafted
+    token with the overlap of the two distributions) but not the rule for a
+    tree. This follows recursive rejection sampling (Jeon et al. 2024,
+    "Recursive Speculative Decoding"; SpecInfer's multi-step speculative
+    sampling extended to siblings drawn without replacement):
+
+    at the current node (starting at the root), with p = softmax(target / T)
+    and q = softmax(draft / T) there, its children are tried in index order.
+    Child c with token x is accepted iff u_accept[c] * q(x) < p(x) (i.e. with
+    probability min(1, p(x) / q(x)); q(x) = 0 < p(x) accepts, p(x) = 0
+    rejects); on acceptance the walk moves to c. On rejection p becomes the
+    normalised residual max(0, p - q) (unchanged if that is all zero) and
+    x's mass is removed from q, which is renormalised. A child whose token
+    is outside [0, V) is skipped. When no child is accepted, the bonus token
+    is drawn from the current p by inverse transform in token order: the
+    smallest v with cumsum(p)[v] > u_bonus[b] * sum(p).
+
+    ``target_logits``, ``draft_logits``: [N, V], row i = the next-token
+    logits after node i (the draft's row is the distribution node i's
+    children were drawn from); ``u_accept`` [N], ``u_bonus`` [B] in [0, 1).
+    Returns (accept_len [B], path [B, max_depth+1] local ids root..last
+    accepted then -1, bonus [B], margin [B]); margin is the smallest distance
+    of any decision from its boundary (|u q(x) - p(x)| for a child test, the
+    distance of u_bonus * sum(p) to the nearest cumulative boundary for the
+    bonus), so a test can tell a rounding-level tie from a disagreement.
+    """
+    par = _np(parent, np.int64)
+    tok = _np(draft_tok, np.int64)
+    cu = _np(cu_nodes, np.int64)
+    tl = _np(target_logits, np.float64)
+    dl = _np(draft_logits, np.float64)
+    ua = _np(u_accept, np.float64)
+    ub = _np(u_bonus, np.float64)
+    T = float(temperature)
+    v = tl.shape[1]
+    batch = len(cu) - 1
+    al = np.zeros(batch, np.int32)
+    path = np.full((batch, max_depth + 1), -1, np.int32)
+    bonus = np.zeros(batch, np.int32)
+    margin = np.full(batch, np.inf)
+    for b in range(batch):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        node, depth = 0, 0
+        path[b, 0] = 0
+        while True:
+            p = _dist(tl[lo + node], T)
+            q = _dist(dl[lo + node], T)
+            nxt = None
+            for c in range(node + 1, hi - lo):
+                if par[lo + c] != node:
+                    continue
+                x = int(tok[lo + c])
+                if not 0 <= x < v:
+                    continue
+                lhs, rhs = ua[lo + c] * q[x], p[x]
+                margin[b] = min(margin[b], abs(lhs - rhs))
+                if lhs < rhs:
+                    nxt = c
+                    break
+                r = np.maximum(p - q, 0.0)
+                if r.sum() > 0:
+                    p = r / r.sum()
+                q = q.copy()
+                q[x] = 0.0
+                if q.sum() > 0:
+                    q = q / q.sum()
+            if nxt is None:
+                cdf = np.cumsum(p)
+                t = ub[b] * cdf[-1]
+                k = int(np.searchsorted(cdf, t, side="right"))
+                k = min(k, v - 1)
+                while p[k] == 0 and k > 0:       # u_bonus ~ 1: the last token with mass
+                    k -= 1
+                bonus[b] = k
+                below = cdf[k - 1] if k > 0 else 0.0
+                margin[b] = min(margin[b], t - below, cdf[k] - t)
+                break
+            node = nxt
+            depth += 1
+            if depth <= max_depth:
+                path[b, depth] = node
+        al[b] = depth
+    return al, path, bonus, margin

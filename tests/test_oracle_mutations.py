@@ -57,6 +57,13 @@ def test_planted_oracle_mistake_is_caught(name, tmp_path):
 # before the pins run.
 PY_SRC = os.path.join(ROOT, "oracle", "oracle.py")
 PY_MUTANTS = {
+    "sampled_residual_not_clamped": ("r = np.maximum(p - q, 0.0)", "r = p - q"),
+    "sampled_rejected_token_kept_in_q": ("                q[x] = 0.0\n", ""),
+    "sampled_accept_when_above": ("                if lhs < rhs:", "                if lhs > rhs:"),
+    "sampled_bonus_from_unreduced_target": ("                cdf = np.cumsum(p)",
+                                            "                cdf = np.cumsum(_dist(tl[lo + node], T))"),
+    "sampled_residual_after_q_update": ("                r = np.maximum(p - q, 0.0)\n                if r.sum() > 0:\n                    p = r / r.sum()\n                q = q.copy()\n                q[x] = 0.0\n                if q.sum() > 0:\n                    q = q / q.sum()\n",
+                                        "                q = q.copy()\n                q[x] = 0.0\n                if q.sum() > 0:\n                    q = q / q.sum()\n                r = np.maximum(p - q, 0.0)\n                if r.sum() > 0:\n                    p = r / r.sum()\n"),
     "e2e_max_instead_of_min": ("alpha[i] = np.minimum(p, q).sum()", "alpha[i] = np.maximum(p, q).sum() - 1.0"),
     "e2e_no_temperature": ("d = _np(draft_logits, np.float64) / float(temperature)",
                            "d = _np(draft_logits, np.float64)"),
@@ -72,7 +79,7 @@ PY_MUTANTS = {
 
 
 def _run_pins_with_python_oracle(tmp_path, old=None, new=None):
-    """Run the E2E-TV and Graft pins against a copy of the oracle package (optionally
+    """Run the E2E-TV, Graft and sampled-acceptance pins against a copy of the oracle package (optionally
     mutated); returns pytest's exit code (0 all passed, 1 some failed)."""
     import shutil
     pkg = tmp_path / "oracle"
@@ -86,7 +93,7 @@ def _run_pins_with_python_oracle(tmp_path, old=None, new=None):
             "spec = importlib.util.spec_from_file_location('oracle', %r, submodule_search_locations=[%r])\n"
             "m = importlib.util.module_from_spec(spec); sys.modules['oracle'] = m; spec.loader.exec_module(m)\n"
             "import pytest\n"
-            "sys.exit(pytest.main(['-x', '-q', '-p', 'no:cacheprovider', '-k', 'e2e or graft', %r]))\n"
+            "sys.exit(pytest.main(['-x', '-q', '-p', 'no:cacheprovider', '-k', 'e2e or graft or sampled', %r]))\n"
             % (str(pkg / "__init__.py"), str(pkg), os.path.join(ROOT, "tests", "test_oracle_pins.py")))
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
                        timeout=300)

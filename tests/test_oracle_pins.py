@@ -625,3 +625,193 @@ def test_graft_update_then_retrieve_follows_the_new_rows(oracle_lib):
     lg[2, 13] = 1.0
     adj = oracle.graft_update(adj, lg, [10, 11, 12])
     assert oracle.graft_retrieve(adj, [10], [-1, 0, 1], [0, 0, 0])[0].tolist() == [11, 12, 13]
+
+
+# ---------------------------------------------------------------------------
+# Stochastic tree verification (recursive rejection sampling; the pages run at
+# T = 1 -- BlockPilot §五, D-cut §4 -- and fix the one-token rule, SpecOPD
+# §03.2). The defining property of speculative sampling is that the emitted
+# tokens follow the target's distributions whatever the draft was; the pins
+# check that property by sampling, the greedy limit against the C oracle,
+# and closed forms.
+
+def _chi2(counts, probs):
+    counts = np.asarray(counts, np.float64)
+    exp = probs * counts.sum()
+    keep = exp > 0
+    assert np.all(counts[~keep] == 0)
+    return float(((counts[keep] - exp[keep]) ** 2 / exp[keep]).sum())
+
+
+def _rrs_trials(rng, n_trials, v=6, width=(3, 2)):
+    """Trees drawn the way a draft model draws them: the root's children are
+    `width[0]` distinct tokens sampled from the draft's q at the root without
+    replacement, each child's children `width[1]` tokens from q at that child.
+    The target's and the draft's next-token logits depend on the token a node
+    carries (a toy model with one step of context)."""
+    t_root, d_root = rng.normal(0, 1.2, v), rng.normal(0, 1.2, v)
+    t_tok, d_tok = rng.normal(0, 1.2, (v, v)), rng.normal(0, 1.2, (v, v))
+    q_root = np.exp(d_root) / np.exp(d_root).sum()
+    q_tok = np.exp(d_tok) / np.exp(d_tok).sum(1, keepdims=True)
+    par, tok, tl, dl, cu = [], [], [], [], [0]
+    for _ in range(n_trials):
+        kids = rng.choice(v, size=width[0], replace=False, p=q_root)
+        nodes = [(-1, 0, t_root, d_root)]
+        for a in kids:
+            nodes.append((0, int(a), t_tok[a], d_tok[a]))
+        for ci, a in enumerate(kids):
+            for g in rng.choice(v, size=width[1], replace=False, p=q_tok[a]):
+                nodes.append((1 + ci, int(g), t_tok[g], d_tok[g]))
+        for pp, tk, t, d in nodes:
+            par.append(pp)
+            tok.append(tk)
+            tl.append(t)
+            dl.append(d)
+        cu.append(len(par))
+    n = len(par)
+    return (np.array(par, np.int32), np.array(tok, np.int32), np.array(cu, np.int32),
+            np.array(tl), np.array(dl), rng.random(n), rng.random(n_trials), t_root, t_tok)
+
+
+def _first_two_tokens(tok, cu, al, path, bonus):
+    first, second = [], []
+    for b in range(len(cu) - 1):
+        lo = cu[b]
+        toks = [tok[lo + path[b, d]] for d in range(1, al[b] + 1)] + [bonus[b]]
+        first.append(toks[0])
+        second.append(toks[1] if al[b] >= 1 else -1)
+    return np.array(first), np.array(second)
+
+
+def test_sampled_emitted_tokens_follow_the_target():
+    rng = np.random.default_rng(31)
+    v, n = 6, 12000
+    par, tok, cu, tl, dl, ua, ub, t_root, t_tok = _rrs_trials(rng, n, v)
+    al, path, bonus, _ = oracle.accept_sampled(par, tok, cu, tl, dl, 1.0, ua, ub, max_depth=2)
+    first, second = _first_two_tokens(tok, cu, al, path, bonus)
+    p_root = np.exp(t_root) / np.exp(t_root).sum()
+    # 5 degrees of freedom: 40 is far beyond the 1e-6 quantile (35.9)
+    assert _chi2(np.bincount(first, minlength=v), p_root) < 40
+    # after an accepted child carrying token a, the next token follows the
+    # target's distribution at that child
+    tested = 0
+    for a in range(v):
+        sel = (al >= 1) & (first == a)
+        if sel.sum() < 400:
+            continue
+        p_a = np.exp(t_tok[a]) / np.exp(t_tok[a]).sum()
+        assert _chi2(np.bincount(second[sel], minlength=v), p_a) < 40, a
+        tested += 1
+    assert tested >= 3
+
+
+def test_sampled_reduces_to_greedy_acceptance_as_temperature_vanishes(oracle_lib):
+    rng = np.random.default_rng(32)
+    v, batch = 40, 30
+    par, tok, cu = [], [], [0]
+    for b in range(batch):
+        n = int(rng.integers(1, 24))
+        p = [-1] + [int(rng.integers(0, i)) for i in range(1, n)]
+        t = [int(rng.integers(0, v))]
+        for i in range(1, n):             # siblings carry distinct tokens
+            used = {t[j] for j in range(1, i) if p[j] == p[i]}
+            t.append(int(rng.choice([x for x in range(v) if x not in used])))
+        par += p
+        tok += t
+        cu.append(len(par))
+    n = len(par)
+    tl = rng.normal(0, 3, (n, v))
+    dl = rng.normal(0, 3, (n, v))
+    # make many children agree with the target's argmax so that paths go deep
+    for b in range(batch):
+        lo, hi = cu[b], cu[b + 1]
+        for c in range(lo + 1, hi):
+            if rng.random() < 0.6:
+                tl[lo + par[c], tok[c]] = tl[lo + par[c]].max() + 1.0
+    target_tok = tl.argmax(1).astype(np.int32)
+    al_g, path_g, bonus_g = oracle.accept(par, tok, target_tok, cu, max_depth=24)
+    al, path, bonus, _ = oracle.accept_sampled(par, tok, cu, tl, dl, 1e-6, rng.random(n),
+                                               rng.random(batch), max_depth=24)
+    np.testing.assert_array_equal(al, al_g)
+    np.testing.assert_array_equal(path, path_g)
+    np.testing.assert_array_equal(bonus, bonus_g)
+    assert al.max() >= 3
+
+
+def test_sampled_one_child_is_accepted_with_probability_min_1_p_over_q():
+    # two tokens: p = (a, 1-a), q = (c, 1-c); the root's one child carries
+    # token 0. Over a grid of uniforms it is accepted for a fraction
+    # min(1, a/c) of them; on rejection the residual is all on token 1.
+    for a, c in ((0.3, 0.6), (0.6, 0.3), (0.25, 0.25)):
+        grid = (np.arange(1000) + 0.5) / 1000
+        n = len(grid)
+        par = np.tile([-1, 0], n).astype(np.int32)
+        tok = np.tile([5, 0], n).astype(np.int32)
+        cu = np.arange(0, 2 * n + 1, 2).astype(np.int32)
+        tl = np.tile([[np.log(a), np.log(1 - a)], [0.0, 0.0]], (n, 1))
+        dl = np.tile([[np.log(c), np.log(1 - c)], [0.0, 0.0]], (n, 1))
+        ua = np.zeros(2 * n)
+        ua[1::2] = grid
+        al, path, bonus, _ = oracle.accept_sampled(par, tok, cu, tl, dl, 1.0, ua,
+                                                   np.full(n, 0.5), max_depth=1)
+        assert abs(al.mean() - min(1.0, a / c)) <= 1.5e-3
+        assert np.all(bonus[al == 0] == 1)        # residual max(0, p - q) sits on token 1
+        assert np.all(path[al == 1, 1] == 1)
+
+
+def test_sampled_bonus_is_inverse_transform_sampling():
+    # a lone root: the bonus is drawn from p; over a uniform grid of K points
+    # token v comes up K * p(v) times, up to one point per boundary
+    rng = np.random.default_rng(33)
+    v, k = 9, 3000
+    logits = rng.normal(0, 1.5, v)
+    logits[4] = -np.inf                        # a token with no mass is never drawn
+    p = np.exp(logits - logits.max())
+    p /= p.sum()
+    grid = (np.arange(k) + 0.5) / k
+    par = np.full(k, -1, np.int32)
+    cu = np.arange(k + 1, dtype=np.int32)
+    al, _, bonus, _ = oracle.accept_sampled(par, np.zeros(k, np.int32), cu, np.tile(logits, (k, 1)),
+                                            np.zeros((k, v)), 1.0, np.zeros(k), grid, max_depth=0)
+    assert np.all(al == 0)
+    counts = np.bincount(bonus, minlength=v)
+    assert counts[4] == 0
+    assert np.all(np.abs(counts - k * p) <= 1.0 + 1e-9)
+    assert np.all(np.diff(bonus) >= 0)         # token order: the grid is increasing
+
+
+def test_sampled_draft_equal_to_target_takes_every_first_child():
+    # q = p: every tried child has ratio 1, so the first child is always taken
+    rng = np.random.default_rng(34)
+    v = 12
+    par = np.array([-1, 0, 0, 1, 1, 3, 2], np.int32)
+    tok = np.array([0, 3, 4, 5, 6, 7, 8], np.int32)
+    tl = rng.normal(0, 1, (7, v))
+    tl[5] = -30.0
+    tl[5, 9] = 30.0                            # the leaf's target is sure of token 9
+    ua = rng.random(7) * 0.999
+    al, path, bonus, _ = oracle.accept_sampled(par, tok, [0, 7], tl, tl.copy(), 1.0, ua, [0.7],
+                                               max_depth=4)
+    assert al[0] == 3 and path[0].tolist() == [0, 1, 3, 5, -1] and bonus[0] == 9
+
+
+def test_sampled_temperature_scales_the_logits_and_bad_tokens_are_skipped():
+    rng = np.random.default_rng(35)
+    par, tok, cu, tl, dl, ua, ub, _, _ = _rrs_trials(rng, 200, 8)
+    a = oracle.accept_sampled(par, tok, cu, tl, dl, 0.7, ua, ub, max_depth=2)
+    b = oracle.accept_sampled(par, tok, cu, tl / 0.7, dl / 0.7, 1.0, ua, ub, max_depth=2)
+    for x, y in zip(a[:3], b[:3]):
+        np.testing.assert_array_equal(x, y)
+    # children whose token is outside the vocabulary are passed over: with
+    # every root child out of range the result is that of a lone root
+    bad = tok.copy()
+    kids = np.where(par == 0)[0]
+    bad[kids] = -1
+    bad[kids[::2]] = 8
+    al, _, bonus, _ = oracle.accept_sampled(par, bad, cu, tl, dl, 1.0, ua, ub, max_depth=2)
+    roots = cu[:-1]
+    al1, _, bonus1, _ = oracle.accept_sampled(np.full(len(roots), -1, np.int32), tok[roots],
+                                              np.arange(len(roots) + 1, dtype=np.int32),
+                                              tl[roots], dl[roots], 1.0, ua[roots], ub, max_depth=0)
+    assert np.all(al == 0) and np.all(al1 == 0)
+    np.testing.assert_array_equal(bonus, bonus1)
