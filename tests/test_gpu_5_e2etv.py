@@ -71,6 +71,27 @@ def test_unaligned_and_ragged_vocabularies(v, offset, dtype):
     _check(t, d, [0, 5, 5, 12], dtype=dtype, offset=offset)     # includes an empty branch
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_masked_vocabulary_entries(dtype):
+    # -inf logits (a masked vocabulary) carry no probability: long masked runs,
+    # a row masked everywhere but a few tokens, and masks that differ between
+    # the target and the draft
+    rng = np.random.default_rng(5)
+    v = 151936
+    t, d = _logits(rng, 6, v)
+    t[0, : v // 2] = -np.inf
+    d[0, : v // 2] = -np.inf
+    t[1, 1000:] = -np.inf
+    d[1, 5000:] = -np.inf
+    t[2, rng.random(v) < 0.9] = -np.inf
+    keep = rng.choice(v, 5, replace=False)
+    mask = np.ones(v, bool)
+    mask[keep] = False
+    t[3, mask] = -np.inf
+    d[4, : 3 * v // 4] = -np.inf
+    _check(t, d, [0, 6], dtype=dtype)
+
+
 def test_identical_and_disjoint_distributions():
     rng = np.random.default_rng(4)
     t, _ = _logits(rng, 4, 2048)

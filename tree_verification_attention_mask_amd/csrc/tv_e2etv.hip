@@ -16,7 +16,7 @@
 //           exp2 per vocabulary entry. The second pass re-reads rows the
 //           first pass just brought through L2 / the last-level cache.
 // branch_kernel: one thread per branch, prefix products and their sum.
-#include "tv_launch.h"
+#include "tv_vocab.h"
 
 namespace tv {
 namespace {
@@ -26,91 +26,13 @@ constexpr int kTvWaves = kTvThreads / 64;
 constexpr int kUnroll = 4;  // 16-byte groups per row each thread keeps in flight
 constexpr float kLog2eF = 1.4426950408889634f;
 
-struct MaxSum {
-  float m, s;  // log2-domain max and sum of 2^(y - m)
-};
-__device__ __forceinline__ MaxSum merge(MaxSum a, MaxSum b) {
-  const float m = fmaxf(a.m, b.m);
-  if (m == -INFINITY) return MaxSum{m, 0.f};
-  return MaxSum{m, a.s * __builtin_amdgcn_exp2f(a.m - m) + b.s * __builtin_amdgcn_exp2f(b.m - m)};
-}
-// fold a group of raw logits x into a running (max, sum) of y = c x (log2
-// units, c = log2(e) / T > 0, so the max of y is c times the max of x)
-template <int N>
-__device__ __forceinline__ void fold(MaxSum& r, const float (&x)[N], float c) {
-  float mx = x[0];
-#pragma unroll
-  for (int i = 1; i < N; ++i) mx = fmaxf(mx, x[i]);
-  const float m = fmaxf(r.m, mx * c);
-  float acc = (r.m == -INFINITY) ? 0.f : r.s * __builtin_amdgcn_exp2f(r.m - m);
-#pragma unroll
-  for (int i = 0; i < N; ++i) acc += __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], c, -m));
-  r = MaxSum{m, acc};
-}
-
-// Block-wide merge of one value per thread; every thread gets the result.
-__device__ MaxSum block_merge(MaxSum v, MaxSum* s_red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    MaxSum o{__shfl_xor(v.m, off, 64), __shfl_xor(v.s, off, 64)};
-    v = merge(v, o);
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) s_red[wave] = v;
-  __syncthreads();
-  MaxSum r = s_red[0];
-#pragma unroll
-  for (int w = 1; w < kTvWaves; ++w) r = merge(r, s_red[w]);
-  __syncthreads();
-  return r;
-}
-__device__ float block_sum(float v, float* s_red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) s_red[wave] = v;
-  __syncthreads();
-  float r = 0.f;
-#pragma unroll
-  for (int w = 0; w < kTvWaves; ++w) r += s_red[w];
-  __syncthreads();
-  return r;
-}
-
-// Values of a row in groups of W (16-byte loads when VEC), converted to fp32.
-template <typename T>
-struct Row;
-template <>
-struct Row<__bf16> {
-  static constexpr int W = 8;
-  __device__ static void load(const __bf16* p, float (&y)[W]) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      y[2 * i] = __uint_as_float(w[i] << 16);
-      y[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-  }
-  __device__ static float one(const __bf16* p) { return static_cast<float>(*p); }
-};
-template <>
-struct Row<float> {
-  static constexpr int W = 4;
-  __device__ static void load(const float* p, float (&y)[W]) {
-    const float4 u = *reinterpret_cast<const float4*>(p);
-    y[0] = u.x; y[1] = u.y; y[2] = u.z; y[3] = u.w;
-  }
-  __device__ static float one(const float* p) { return *p; }
-};
-
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kTvThreads) void alpha_kernel(const T* __restrict__ tl,
                                                            const T* __restrict__ dl, int64_t vocab,
                                                            float c, float* __restrict__ alpha) {
   __shared__ MaxSum s_ms[kTvWaves];
   __shared__ float s_f[kTvWaves];
-  constexpr int W = Row<T>::W;
+  constexpr int W = VocabUnit<T, true>::W;
   const int64_t node = blockIdx.x;
   const T* a = tl + node * vocab;
   const T* b = dl + node * vocab;
@@ -125,8 +47,8 @@ __global__ __launch_bounds__(kTvThreads) void alpha_kernel(const T* __restrict__
     float ya[kUnroll][W], yb[kUnroll][W];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      Row<T>::load(a + (j + u * kTvThreads) * W, ya[u]);
-      Row<T>::load(b + (j + u * kTvThreads) * W, yb[u]);
+      VocabUnit<T, true>::load(a + (j + u * kTvThreads) * W, ya[u]);
+      VocabUnit<T, true>::load(b + (j + u * kTvThreads) * W, yb[u]);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -136,18 +58,18 @@ __global__ __launch_bounds__(kTvThreads) void alpha_kernel(const T* __restrict__
   }
   for (; j < nvec; j += kTvThreads) {
     float ya[W], yb[W];
-    Row<T>::load(a + j * W, ya);
-    Row<T>::load(b + j * W, yb);
+    VocabUnit<T, true>::load(a + j * W, ya);
+    VocabUnit<T, true>::load(b + j * W, yb);
     fold(ra, ya, c);
     fold(rb, yb, c);
   }
   for (int64_t v = tail0 + tid; v < vocab; v += kTvThreads) {
-    const float ya[1] = {Row<T>::one(a + v)}, yb[1] = {Row<T>::one(b + v)};
+    const float ya[1] = {load_one<T>(a + v)}, yb[1] = {load_one<T>(b + v)};
     fold(ra, ya, c);
     fold(rb, yb, c);
   }
-  ra = block_merge(ra, s_ms);
-  rb = block_merge(rb, s_ms);
+  ra = block_merge<kTvWaves>(ra, s_ms);
+  rb = block_merge<kTvWaves>(rb, s_ms);
   const float La = ra.m + __log2f(ra.s), Lb = rb.m + __log2f(rb.s);
 
   // pass 2
@@ -162,22 +84,22 @@ __global__ __launch_bounds__(kTvThreads) void alpha_kernel(const T* __restrict__
     float ya[kUnroll][W], yb[kUnroll][W];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      Row<T>::load(a + (j + u * kTvThreads) * W, ya[u]);
-      Row<T>::load(b + (j + u * kTvThreads) * W, yb[u]);
+      VocabUnit<T, true>::load(a + (j + u * kTvThreads) * W, ya[u]);
+      VocabUnit<T, true>::load(b + (j + u * kTvThreads) * W, yb[u]);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) overlap(ya[u], yb[u]);
   }
   for (; j < nvec; j += kTvThreads) {
     float ya[W], yb[W];
-    Row<T>::load(a + j * W, ya);
-    Row<T>::load(b + j * W, yb);
+    VocabUnit<T, true>::load(a + j * W, ya);
+    VocabUnit<T, true>::load(b + j * W, yb);
     overlap(ya, yb);
   }
   for (int64_t v = tail0 + tid; v < vocab; v += kTvThreads)
-    acc += __builtin_amdgcn_exp2f(fminf(__builtin_fmaf(Row<T>::one(a + v), c, -La),
-                                        __builtin_fmaf(Row<T>::one(b + v), c, -Lb)));
-  acc = block_sum(acc, s_f);
+    acc += __builtin_amdgcn_exp2f(fminf(__builtin_fmaf(load_one<T>(a + v), c, -La),
+                                        __builtin_fmaf(load_one<T>(b + v), c, -Lb)));
+  acc = block_sum<kTvWaves>(acc, s_f);
   if (tid == 0) alpha[node] = acc;
 }
 
@@ -202,9 +124,7 @@ hipError_t run_alpha(const void* tl, const void* dl, int32_t n, int32_t vocab, f
                      float* alpha, hipStream_t stream) {
   const T* a = static_cast<const T*>(tl);
   const T* b = static_cast<const T*>(dl);
-  constexpr int W = Row<T>::W;
-  const bool vec = (vocab % W) == 0 && (reinterpret_cast<uintptr_t>(a) & 15) == 0 &&
-                   (reinterpret_cast<uintptr_t>(b) & 15) == 0;
+  const bool vec = vocab_vec<T>(a, vocab) && vocab_vec<T>(b, vocab);
   if (vec)
     hipLaunchKernelGGL((alpha_kernel<T, true>), dim3(n), dim3(kTvThreads), 0, stream, a, b,
                        (int64_t)vocab, c, alpha);

@@ -24,7 +24,7 @@
 //   waves' lists; the merge kernel ranks the shares' lists and writes the
 //   row. A row is written only when no later node carries the same token,
 //   so every row has one writer.
-#include "tv_launch.h"
+#include "tv_vocab.h"
 
 namespace tv {
 namespace {
@@ -87,36 +87,6 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 
-// Values of a logits row: 16-byte groups when the rows are aligned, else one at a time.
-template <typename T, bool VEC>
-struct Unit;
-template <>
-struct Unit<__bf16, true> {
-  static constexpr int W = 8;
-  __device__ static void load(const __bf16* p, float (&y)[W]) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      y[2 * i] = __uint_as_float(w[i] << 16);
-      y[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-  }
-};
-template <>
-struct Unit<float, true> {
-  static constexpr int W = 4;
-  __device__ static void load(const float* p, float (&y)[W]) {
-    const float4 u = *reinterpret_cast<const float4*>(p);
-    y[0] = u.x; y[1] = u.y; y[2] = u.z; y[3] = u.w;
-  }
-};
-template <typename T>
-struct Unit<T, false> {
-  static constexpr int W = 1;
-  __device__ static void load(const T* p, float (&y)[W]) { y[0] = static_cast<float>(*p); }
-};
-
 // Whether this node writes its token's row: the token is in range and no later
 // node carries it. Uniform over the block (every thread reads the same token).
 __device__ bool owns_row(const int32_t* node_tokens, int num_nodes, int node, int tok, int vocab) {
@@ -136,7 +106,7 @@ __global__ __launch_bounds__(kUpdateThreads) void graft_topk_kernel(
     int32_t* __restrict__ adj, int32_t vocab, int32_t k, const T* __restrict__ logits,
     int32_t num_nodes, const int32_t* __restrict__ node_tokens, int32_t splits,
     int2* __restrict__ part) {
-  constexpr int UW = Unit<T, VEC>::W;
+  constexpr int UW = VocabUnit<T, VEC>::W;
   __shared__ float s_v[kUpdateWaves * 16];
   __shared__ int s_i[kUpdateWaves * 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -192,7 +162,7 @@ __global__ __launch_bounds__(kUpdateThreads) void graft_topk_kernel(
     float y[kUpdateUnroll][UW];
 #pragma unroll
     for (int u = 0; u < kUpdateUnroll; ++u)
-      Unit<T, VEC>::load(row + min((int64_t)(u * kUpdateThreads + tid), n - 1) * UW, y[u]);
+      VocabUnit<T, VEC>::load(row + min((int64_t)(u * kUpdateThreads + tid), n - 1) * UW, y[u]);
     float lm = -INFINITY;  // max ignores NaN
 #pragma unroll
     for (int u = 0; u < kUpdateUnroll; ++u) {
@@ -222,7 +192,7 @@ __global__ __launch_bounds__(kUpdateThreads) void graft_topk_kernel(
     float y[kUpdateUnroll][UW];
 #pragma unroll
     for (int u = 0; u < kUpdateUnroll; ++u)
-      Unit<T, VEC>::load(row + min(base + u * kUpdateThreads + tid, n - 1) * UW, y[u]);
+      VocabUnit<T, VEC>::load(row + min(base + u * kUpdateThreads + tid, n - 1) * UW, y[u]);
 #pragma unroll
     for (int u = 0; u < kUpdateUnroll; ++u) {
       const int64_t idx = base + u * kUpdateThreads + tid;
@@ -235,7 +205,7 @@ __global__ __launch_bounds__(kUpdateThreads) void graft_topk_kernel(
   for (; base < n_r; base += kUpdateThreads) {
     float y[UW];
     const int64_t idx = base + tid;
-    Unit<T, VEC>::load(row + min(idx, n - 1) * UW, y);
+    VocabUnit<T, VEC>::load(row + min(idx, n - 1) * UW, y);
     const uint64_t vmask = __ballot(idx < n);
     const int uid = (int)((u0 + idx) * UW);
 #pragma unroll
@@ -360,7 +330,7 @@ namespace {
 template <typename T, bool VEC>
 hipError_t run_update(int32_t* adj, int32_t vocab, int32_t k, const T* lg, int32_t num_nodes,
                       const int32_t* node_tokens, int2* part, hipStream_t stream) {
-  const int s = update_splits(num_nodes, vocab / Unit<T, VEC>::W);
+  const int s = update_splits(num_nodes, vocab / VocabUnit<T, VEC>::W);
   hipLaunchKernelGGL((graft_topk_kernel<T, VEC>), dim3(num_nodes, s), dim3(kUpdateThreads), 0,
                      stream, adj, vocab, k, lg, num_nodes, node_tokens, s, part);
   if (s > 1)
@@ -371,8 +341,7 @@ hipError_t run_update(int32_t* adj, int32_t vocab, int32_t k, const T* lg, int32
 }  // namespace
 
 bool graft_update_vec(const void* logits, int32_t dtype, int32_t vocab) {
-  const bool aligned = (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
-  return aligned && vocab % (dtype == TV_BF16 ? 8 : 4) == 0;
+  return dtype == TV_BF16 ? vocab_vec<__bf16>(logits, vocab) : vocab_vec<float>(logits, vocab);
 }
 
 hipError_t launch_graft_update(int32_t* adj, int32_t vocab, int32_t k, const void* logits,
