@@ -347,6 +347,34 @@ def main():
             w.total_nodes, vocab, k_adj)
         next_rows["graft_retrieve_us"] = time_graph(g_ret, RS)
         next_rows["graft_retrieve_shape"] = "1 request, 20-slot template (depth %d)" % 5
+    # Stochastic verification of the same tree at temperature 1: seeded target
+    # and draft logits (N(0, 3^2), draft = target + N(0, 1)), children drawn
+    # from the draft without replacement, seeded uniforms
+    if w.name == W.CONFIG_NAMES[2]:
+        si = W.sampled_inputs(np.random.default_rng(args.config), [list(W.GRAFT_TREE_PARENT)],
+                              W.QWEN3_VOCAB)
+        s_par = torch.from_numpy(si.parent).to(dev)
+        s_tok = torch.from_numpy(si.draft_tok).to(dev)
+        s_cu = torch.from_numpy(si.cu_nodes).to(dev)
+        s_tl = torch.from_numpy(si.target_logits).to(torch.bfloat16).to(dev)
+        s_dl = torch.from_numpy(si.draft_logits).to(torch.bfloat16).to(dev)
+        s_ua = torch.from_numpy(si.u_accept).to(dev)
+        s_ub = torch.from_numpy(si.u_bonus).to(dev)
+        s_ws = torch.empty(max(1, tv.tree_accept_sampled_workspace_size(len(si.parent))),
+                           dtype=torch.uint8, device=dev)
+        s_out = {"accept_len": torch.empty(1, dtype=torch.int32, device=dev),
+                 "path": torch.empty((1, si.max_depth + 1), dtype=torch.int32, device=dev),
+                 "bonus": torch.empty(1, dtype=torch.int32, device=dev)}
+
+        def sampled_call():
+            tv.tree_accept_sampled(s_par, s_tok, s_cu, s_tl, s_dl, s_ua, s_ub, len(si.parent),
+                                   si.max_children, si.max_depth, 1.0, workspace=s_ws, out=s_out)
+        sampled_call()
+        g_s = capture(lambda: [sampled_call() for _ in range(8)])
+        next_rows["accept_sampled_us"] = time_graph(g_s, 8)
+        next_rows["accept_sampled_len"] = int(s_out["accept_len"].item())
+        next_rows["accept_sampled_shape"] = (
+            "60-node Graft tree, 151936-vocab bf16 target and draft logits, T = 1")
     achieved_gbs = alg_bytes / (us_attn * 1e-6) / 1e9
     achieved_tflops = alg_flops / (us_attn * 1e-6) / 1e12
     plan_splits = (need > 0)

@@ -6,6 +6,8 @@
  *   2. tv_tree_verify_attn one target attention layer: every tree node attends
  *                          the request's KV prefix plus its own root path
  *   3. tv_tree_accept      greedy acceptance: longest accepted root-to-leaf path
+ *   3s. tv_tree_accept_sampled  acceptance when sampling (temperature > 0):
+ *                          recursive rejection sampling on both models' logits
  * and, ahead of them for batches of chain drafts,
  *   0. tv_dcut_select      D-cut verification budget: rank the batch's draft
  *                          positions and pack each request's kept prefix
@@ -60,7 +62,7 @@ typedef enum {
   TV_OK = 0,
   TV_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, inconsistent shape */
   TV_ERR_UNSUPPORTED = 2,      /* valid but outside what the kernels implement */
-  TV_ERR_WORKSPACE = 3,        /* workspace_bytes below tv_tree_verify_attn_workspace_size */
+  TV_ERR_WORKSPACE = 3,        /* workspace_bytes below the call's *_workspace_size() */
   TV_ERR_HIP = 4               /* a HIP launch failed */
 } tv_status_t;
 
@@ -339,6 +341,60 @@ size_t tv_graft_update_workspace_size(int32_t num_nodes, int32_t vocab, int32_t 
 tv_status_t tv_graft_update(int32_t* adj, int32_t vocab, int32_t k, const void* target_logits,
                             int32_t dtype, int32_t num_nodes, const int32_t* node_tokens,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * tv_tree_accept_sampled -- stochastic tree verification (sampling at T > 0).
+ *
+ * The pages verify at temperature 1 (BlockPilot §五, D-cut §4) and give the
+ * one-token rule (SpecOPD §03.2: exact rejection sampling accepts a drafted
+ * token with the overlap of the target's and the draft's distributions). The
+ * rule for a tree is recursive rejection sampling (Jeon et al. 2024,
+ * "Recursive Speculative Decoding"), SpecInfer's multi-step speculative
+ * sampling with siblings drawn without replacement, under which the emitted
+ * tokens follow the target's distribution whatever the draft was:
+ *
+ * starting at the root, with p = softmax(target_logits[node] / T) and
+ * q = softmax(draft_logits[node] / T) (NaN logits count as -inf), the node's
+ * children are tried in local index order. The child with token x is
+ * accepted iff u_accept[child] * q(x) < p(x) (probability min(1, p(x)/q(x)));
+ * the walk then moves to it. On a rejection p becomes the normalised residual
+ * max(0, p - q) (unchanged if that is all zero) and x's mass leaves q, which
+ * is renormalised. A child whose token is outside [0, vocab) is passed over.
+ * When no child is accepted, the bonus token is the smallest v with
+ * sum_{w <= v} p(w) > u_bonus[b] * sum_w p(w) (inverse transform in token
+ * order; the last token with mass when rounding leaves none).
+ *
+ *   parent, draft_tok, cu_nodes  as for tv_tree_accept; draft_tok[i] is the
+ *                token node i carries (the root's is not tested)
+ *   max_nodes    (host) >= every request's node count, <= TV_MAX_ACCEPT_NODES
+ *   max_children (host) >= the most children of any node, <= TV_MAX_SAMPLED_CHILDREN
+ *   max_depth    (host) path row length - 1
+ *   target_logits, draft_logits [total_nodes][vocab], dtype TV_BF16 or TV_F32:
+ *                row i = the next-token logits after node i (the draft's row
+ *                is the distribution node i's children were drawn from)
+ *   temperature  > 0 and finite
+ *   u_accept     [total_nodes] uniforms in [0, 1), one per node (a node's own
+ *                test uses its entry); u_bonus [batch] uniforms in [0, 1)
+ *   accept_len   out [batch]; path out [batch][max_depth + 1] local ids root..last
+ *                accepted node, then -1; bonus_tok out [batch] (-1 when the
+ *                request is empty or its distribution has no mass)
+ *   workspace    >= tv_tree_accept_sampled_workspace_size(total_nodes) bytes,
+ *                256-byte aligned: the per-node softmax normalisers. Contents
+ *                on entry are ignored; calls sharing it must not overlap.
+ * Decisions are taken in fp32: a uniform within rounding of its threshold may
+ * go either way. On a malformed tree indices are clamped and nothing is read or
+ * written out of bounds; results are then undefined.
+ */
+#define TV_MAX_SAMPLED_CHILDREN 512
+size_t tv_tree_accept_sampled_workspace_size(int32_t total_nodes);
+tv_status_t tv_tree_accept_sampled(const int32_t* parent, const int32_t* draft_tok,
+                                   const int32_t* cu_nodes, int32_t batch, int32_t total_nodes,
+                                   int32_t max_nodes, int32_t max_children, int32_t max_depth,
+                                   const void* target_logits, const void* draft_logits,
+                                   int32_t dtype, int32_t vocab, float temperature,
+                                   const float* u_accept, const float* u_bonus,
+                                   int32_t* accept_len, int32_t* path, int32_t* bonus_tok,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* tv_status_string(tv_status_t status);

@@ -139,6 +139,30 @@ def test_graft_argument_checks():
     assert u(FAKE, 151936, 8, FAKE, 1, 60, FAKE, FAKE, need - 1, None) == 3
 
 
+def test_sampled_accept_argument_checks():
+    lib = tv.load_library()
+    f = lib.tv_tree_accept_sampled
+    c = ctypes.c_float
+    ok = dict(batch=1, total=4, max_nodes=4, max_children=3, max_depth=3, dtype=1, vocab=10,
+              temp=1.0, ws=FAKE, ws_bytes=1 << 20)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(FAKE, FAKE, FAKE, a["batch"], a["total"], a["max_nodes"], a["max_children"],
+                 a["max_depth"], FAKE, FAKE, a["dtype"], a["vocab"], c(a["temp"]), FAKE, FAKE,
+                 FAKE, FAKE, FAKE, a["ws"], a["ws_bytes"], None)
+    assert call(batch=0) == 0                      # nothing to do
+    assert call(max_depth=-1) == 1
+    assert call(temp=0.0) == 1 and call(temp=float("nan")) == 1 and call(temp=float("inf")) == 1
+    assert call(vocab=0) == 1 and call(dtype=2) == 1
+    assert call(max_nodes=8193) == 2 and call(max_children=513) == 2
+    need = lib.tv_tree_accept_sampled_workspace_size(4)
+    assert need == 256 and lib.tv_tree_accept_sampled_workspace_size(0) == 0
+    assert call(ws=None, ws_bytes=0) == 3 and call(ws_bytes=need - 1) == 3
+    assert call(ws=ctypes.c_void_p(0x1008)) == 1   # not 256-byte aligned
+
+
 def test_product_path_never_touches_the_oracle():
     pkg = os.path.join(ROOT, "tree_verification_attention_mask_amd")
     for dirpath, _, files in os.walk(pkg):

@@ -1,5 +1,5 @@
-"""MI355X (gfx950) tree-verification attention: mask build, verify attention, greedy accept,
-the D-cut verification budget that packs chain drafts ahead of them, and SpecOPD's
+"""MI355X (gfx950) tree-verification attention: mask build, verify attention, greedy accept
+and stochastic (recursive rejection sampling) acceptance, the D-cut verification budget that packs chain drafts ahead of them, and SpecOPD's
 E2E-TV statistics after them, and Graft's retrieval table (template expansion and
 online update).
 
@@ -19,6 +19,8 @@ from .binding import (  # noqa: F401
     load_library,
     mask_struct,
     tree_accept,
+    tree_accept_sampled,
+    tree_accept_sampled_workspace_size,
     tree_mask_build,
     tree_verify_attn,
     verify_attn_workspace_size,

@@ -25,7 +25,8 @@ MAX_ACCEPT_NODES = 8192
 # every symbol the header declares
 EXPORTS = ("tv_tree_mask_build", "tv_tree_verify_attn_workspace_size", "tv_tree_verify_attn",
            "tv_tree_accept", "tv_dcut_select", "tv_e2e_tv_stats", "tv_graft_retrieve",
-           "tv_graft_update_workspace_size", "tv_graft_update", "tv_status_string")
+           "tv_graft_update_workspace_size", "tv_graft_update",
+           "tv_tree_accept_sampled_workspace_size", "tv_tree_accept_sampled", "tv_status_string")
 MAX_DCUT_DRAFT_POSITIONS = 32768
 
 
@@ -73,6 +74,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tv_graft_update_workspace_size.restype = S
     lib.tv_graft_update.argtypes = [P, I, I, P, I, I, P, P, S, P]
     lib.tv_graft_update.restype = ctypes.c_int
+    lib.tv_tree_accept_sampled_workspace_size.argtypes = [I]
+    lib.tv_tree_accept_sampled_workspace_size.restype = S
+    lib.tv_tree_accept_sampled.argtypes = [P, P, P, I, I, I, I, I, P, P, I, I, ctypes.c_float, P, P,
+                                           P, P, P, P, S, P]
+    lib.tv_tree_accept_sampled.restype = ctypes.c_int
     lib.tv_status_string.argtypes = [ctypes.c_int]
     lib.tv_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -208,6 +214,50 @@ def tree_accept(parent: torch.Tensor, draft_tok: torch.Tensor, target_tok: torch
                             _ptr(o["path"]), _ptr(o["bonus"]), _stream(stream))
     _check("tv_tree_accept", st)
     return o["accept_len"], o["path"], o["bonus"]
+
+
+def tree_accept_sampled(parent: torch.Tensor, draft_tok: torch.Tensor, cu_nodes: torch.Tensor,
+                        target_logits: torch.Tensor, draft_logits: torch.Tensor,
+                        u_accept: torch.Tensor, u_bonus: torch.Tensor, max_nodes: int,
+                        max_children: int, max_depth: int, temperature: float = 1.0,
+                        workspace: torch.Tensor | None = None, out: dict | None = None,
+                        stream=None):
+    """Stochastic acceptance (``tv_tree_accept_sampled``): recursive rejection
+    sampling over both models' next-token logits [N, V] (bf16 or fp32) with
+    the given uniforms (fp32, ``u_accept`` [N], ``u_bonus`` [B]).
+
+    Returns (accept_len [B], path [B, max_depth+1], bonus [B]).
+    """
+    lib = load_library()
+    dev = parent.device
+    batch = cu_nodes.numel() - 1
+    n = parent.numel()
+    assert target_logits.shape == draft_logits.shape and target_logits.dim() == 2
+    assert target_logits.shape[0] == n and target_logits.dtype == draft_logits.dtype
+    assert target_logits.is_contiguous() and draft_logits.is_contiguous()
+    assert u_accept.dtype == torch.float32 and u_bonus.dtype == torch.float32
+    assert u_accept.numel() == n and u_bonus.numel() == batch
+    dt = TV_F32 if target_logits.dtype == torch.float32 else TV_BF16
+    o = dict(out or {})
+    o.setdefault("accept_len", torch.empty(batch, dtype=torch.int32, device=dev))
+    o.setdefault("path", torch.empty((batch, max_depth + 1), dtype=torch.int32, device=dev))
+    o.setdefault("bonus", torch.empty(batch, dtype=torch.int32, device=dev))
+    need = int(lib.tv_tree_accept_sampled_workspace_size(n))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.tv_tree_accept_sampled(
+        _ptr(parent), _ptr(draft_tok), _ptr(cu_nodes), batch, n, int(max_nodes), int(max_children),
+        int(max_depth), _ptr(target_logits), _ptr(draft_logits), dt, target_logits.shape[1],
+        float(temperature), _ptr(u_accept), _ptr(u_bonus), _ptr(o["accept_len"]), _ptr(o["path"]),
+        _ptr(o["bonus"]), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("tv_tree_accept_sampled", st)
+    return o["accept_len"], o["path"], o["bonus"]
+
+
+def tree_accept_sampled_workspace_size(total_nodes: int) -> int:
+    """Bytes ``tv_tree_accept_sampled`` needs (the per-node softmax normalisers)."""
+    return int(load_library().tv_tree_accept_sampled_workspace_size(total_nodes))
 
 
 def dcut_select(conf: torch.Tensor, tokens: torch.Tensor, budget: int, out: dict | None = None,

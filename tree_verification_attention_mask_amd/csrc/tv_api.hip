@@ -209,3 +209,37 @@ extern "C" tv_status_t tv_graft_update(int32_t* adj, int32_t vocab, int32_t k,
   return launched(launch_graft_update(adj, vocab, k, target_logits, dtype, num_nodes, node_tokens,
                                       workspace, stream));
 }
+
+extern "C" size_t tv_tree_accept_sampled_workspace_size(int32_t total_nodes) {
+  return total_nodes > 0 ? sampled_workspace(total_nodes) : 0;
+}
+
+extern "C" tv_status_t tv_tree_accept_sampled(
+    const int32_t* parent, const int32_t* draft_tok, const int32_t* cu_nodes, int32_t batch,
+    int32_t total_nodes, int32_t max_nodes, int32_t max_children, int32_t max_depth,
+    const void* target_logits, const void* draft_logits, int32_t dtype, int32_t vocab,
+    float temperature, const float* u_accept, const float* u_bonus, int32_t* accept_len,
+    int32_t* path, int32_t* bonus_tok, void* workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+  if (batch < 0 || total_nodes < 0 || max_nodes < 0 || max_children < 0 || max_depth < 0)
+    return TV_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return TV_OK;
+  if (!parent || !draft_tok || !cu_nodes || !target_logits || !draft_logits || !u_accept ||
+      !u_bonus || !accept_len || !path || !bonus_tok)
+    return TV_ERR_INVALID_ARGUMENT;
+  if (vocab < 1 || !(temperature > 0.f) || !(temperature < 3.0e38f))
+    return TV_ERR_INVALID_ARGUMENT;
+  if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_INVALID_ARGUMENT;
+  if (max_nodes > TV_MAX_ACCEPT_NODES || max_children > TV_MAX_SAMPLED_CHILDREN)
+    return TV_ERR_UNSUPPORTED;
+  if ((int64_t)total_nodes * vocab > INT64_C(1) << 40) return TV_ERR_UNSUPPORTED;
+  const size_t need = total_nodes > 0 ? sampled_workspace(total_nodes) : 0;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return TV_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255) return TV_ERR_INVALID_ARGUMENT;
+  }
+  return launched(launch_accept_sampled(parent, draft_tok, cu_nodes, batch, total_nodes, max_nodes,
+                                        max_children, max_depth, target_logits, draft_logits,
+                                        dtype, vocab, temperature, u_accept, u_bonus, accept_len,
+                                        path, bonus_tok, workspace, stream));
+}

@@ -39,4 +39,16 @@ hipError_t launch_graft_update(int32_t* adj, int32_t vocab, int32_t k, const voi
                                int32_t dtype, int32_t num_nodes, const int32_t* node_tokens,
                                void* workspace, hipStream_t stream);
 
+// stochastic tree verification: per-node softmax normalisers (workspace),
+// then one walk per request
+size_t sampled_workspace(int32_t total_nodes);
+hipError_t launch_accept_sampled(const int32_t* parent, const int32_t* draft_tok,
+                                 const int32_t* cu_nodes, int32_t batch, int32_t total_nodes,
+                                 int32_t max_nodes, int32_t max_children, int32_t max_depth,
+                                 const void* target_logits, const void* draft_logits,
+                                 int32_t dtype, int32_t vocab, float temperature,
+                                 const float* u_accept, const float* u_bonus,
+                                 int32_t* accept_len, int32_t* path, int32_t* bonus_tok,
+                                 void* workspace, hipStream_t stream);
+
 }  // namespace tv
