@@ -360,7 +360,8 @@ def main():
         s_dl = torch.from_numpy(si.draft_logits).to(torch.bfloat16).to(dev)
         s_ua = torch.from_numpy(si.u_accept).to(dev)
         s_ub = torch.from_numpy(si.u_bonus).to(dev)
-        s_ws = torch.empty(max(1, tv.tree_accept_sampled_workspace_size(len(si.parent))),
+        s_ws = torch.empty(max(1, tv.tree_accept_sampled_workspace_size(
+            len(si.parent), si.max_children, W.QWEN3_VOCAB)),
                            dtype=torch.uint8, device=dev)
         s_out = {"accept_len": torch.empty(1, dtype=torch.int32, device=dev),
                  "path": torch.empty((1, si.max_depth + 1), dtype=torch.int32, device=dev),

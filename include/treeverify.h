@@ -378,15 +378,19 @@ tv_status_t tv_graft_update(int32_t* adj, int32_t vocab, int32_t k, const void* 
  *   accept_len   out [batch]; path out [batch][max_depth + 1] local ids root..last
  *                accepted node, then -1; bonus_tok out [batch] (-1 when the
  *                request is empty or its distribution has no mass)
- *   workspace    >= tv_tree_accept_sampled_workspace_size(total_nodes) bytes,
- *                256-byte aligned: the per-node softmax normalisers. Contents
- *                on entry are ignored; calls sharing it must not overlap.
+ *   workspace    >= tv_tree_accept_sampled_workspace_size(total_nodes, max_children,
+ *                vocab) bytes, 256-byte aligned: per-node normalisers, children
+ *                and rejection steps, and per-share partial sums. Contents on
+ *                entry are ignored; calls sharing it must not overlap.
+ * Launches max_children + 3 kernels (every node's rejection chain is prepared
+ * for all nodes at once, then one walk per request).
  * Decisions are taken in fp32: a uniform within rounding of its threshold may
  * go either way. On a malformed tree indices are clamped and nothing is read or
  * written out of bounds; results are then undefined.
  */
 #define TV_MAX_SAMPLED_CHILDREN 512
-size_t tv_tree_accept_sampled_workspace_size(int32_t total_nodes);
+size_t tv_tree_accept_sampled_workspace_size(int32_t total_nodes, int32_t max_children,
+                                             int32_t vocab);
 tv_status_t tv_tree_accept_sampled(const int32_t* parent, const int32_t* draft_tok,
                                    const int32_t* cu_nodes, int32_t batch, int32_t total_nodes,
                                    int32_t max_nodes, int32_t max_children, int32_t max_depth,

@@ -157,8 +157,10 @@ def test_sampled_accept_argument_checks():
     assert call(temp=0.0) == 1 and call(temp=float("nan")) == 1 and call(temp=float("inf")) == 1
     assert call(vocab=0) == 1 and call(dtype=2) == 1
     assert call(max_nodes=8193) == 2 and call(max_children=513) == 2
-    need = lib.tv_tree_accept_sampled_workspace_size(4)
-    assert need == 256 and lib.tv_tree_accept_sampled_workspace_size(0) == 0
+    need = lib.tv_tree_accept_sampled_workspace_size(4, 3, 10)
+    assert need > 0 and need % 256 == 0
+    assert lib.tv_tree_accept_sampled_workspace_size(0, 3, 10) == 0
+    assert lib.tv_tree_accept_sampled_workspace_size(60, 4, 151936) > need
     assert call(ws=None, ws_bytes=0) == 3 and call(ws_bytes=need - 1) == 3
     assert call(ws=ctypes.c_void_p(0x1008)) == 1   # not 256-byte aligned
 

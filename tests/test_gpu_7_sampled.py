@@ -160,6 +160,8 @@ def test_edge_cases():
     si.target_logits[lo[3] + 2, :] = np.nan      # NaN logits count as -inf
     si.target_logits[lo[3] + 2, 5] = 1.0
     si.draft_logits[lo[3] + 3, : v // 2] = -np.inf
+    si.draft_logits[lo[3] + 1, ::5] = np.nan     # NaN draft logits: no draft mass there
+    si.draft_logits[lo[2], 1::3] = np.nan
     si.u_accept[lo[3] + 1: lo[3] + 7] = 0.0      # the chain is taken as far as mass allows
     got, ref = _run(si)
     _compare(got, ref, max_ties=0)

@@ -74,7 +74,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tv_graft_update_workspace_size.restype = S
     lib.tv_graft_update.argtypes = [P, I, I, P, I, I, P, P, S, P]
     lib.tv_graft_update.restype = ctypes.c_int
-    lib.tv_tree_accept_sampled_workspace_size.argtypes = [I]
+    lib.tv_tree_accept_sampled_workspace_size.argtypes = [I, I, I]
     lib.tv_tree_accept_sampled_workspace_size.restype = S
     lib.tv_tree_accept_sampled.argtypes = [P, P, P, I, I, I, I, I, P, P, I, I, ctypes.c_float, P, P,
                                            P, P, P, P, S, P]
@@ -242,7 +242,8 @@ def tree_accept_sampled(parent: torch.Tensor, draft_tok: torch.Tensor, cu_nodes:
     o.setdefault("accept_len", torch.empty(batch, dtype=torch.int32, device=dev))
     o.setdefault("path", torch.empty((batch, max_depth + 1), dtype=torch.int32, device=dev))
     o.setdefault("bonus", torch.empty(batch, dtype=torch.int32, device=dev))
-    need = int(lib.tv_tree_accept_sampled_workspace_size(n))
+    need = int(lib.tv_tree_accept_sampled_workspace_size(n, int(max_children),
+                                                         target_logits.shape[1]))
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -255,9 +256,10 @@ def tree_accept_sampled(parent: torch.Tensor, draft_tok: torch.Tensor, cu_nodes:
     return o["accept_len"], o["path"], o["bonus"]
 
 
-def tree_accept_sampled_workspace_size(total_nodes: int) -> int:
-    """Bytes ``tv_tree_accept_sampled`` needs (the per-node softmax normalisers)."""
-    return int(load_library().tv_tree_accept_sampled_workspace_size(total_nodes))
+def tree_accept_sampled_workspace_size(total_nodes: int, max_children: int, vocab: int) -> int:
+    """Bytes ``tv_tree_accept_sampled`` needs for these shapes."""
+    return int(load_library().tv_tree_accept_sampled_workspace_size(total_nodes, max_children,
+                                                                     vocab))
 
 
 def dcut_select(conf: torch.Tensor, tokens: torch.Tensor, budget: int, out: dict | None = None,

@@ -210,8 +210,10 @@ extern "C" tv_status_t tv_graft_update(int32_t* adj, int32_t vocab, int32_t k,
                                       workspace, stream));
 }
 
-extern "C" size_t tv_tree_accept_sampled_workspace_size(int32_t total_nodes) {
-  return total_nodes > 0 ? sampled_workspace(total_nodes) : 0;
+extern "C" size_t tv_tree_accept_sampled_workspace_size(int32_t total_nodes, int32_t max_children,
+                                                        int32_t vocab) {
+  if (total_nodes <= 0 || max_children < 0 || vocab < 1) return 0;
+  return sampled_layout(total_nodes, max_children, vocab).total;
 }
 
 extern "C" tv_status_t tv_tree_accept_sampled(
@@ -233,7 +235,7 @@ extern "C" tv_status_t tv_tree_accept_sampled(
   if (max_nodes > TV_MAX_ACCEPT_NODES || max_children > TV_MAX_SAMPLED_CHILDREN)
     return TV_ERR_UNSUPPORTED;
   if ((int64_t)total_nodes * vocab > INT64_C(1) << 40) return TV_ERR_UNSUPPORTED;
-  const size_t need = total_nodes > 0 ? sampled_workspace(total_nodes) : 0;
+  const size_t need = total_nodes > 0 ? sampled_layout(total_nodes, max_children, vocab).total : 0;
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return TV_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) & 255) return TV_ERR_INVALID_ARGUMENT;

@@ -39,9 +39,13 @@ hipError_t launch_graft_update(int32_t* adj, int32_t vocab, int32_t k, const voi
                                int32_t dtype, int32_t num_nodes, const int32_t* node_tokens,
                                void* workspace, hipStream_t stream);
 
-// stochastic tree verification: per-node softmax normalisers (workspace),
-// then one walk per request
-size_t sampled_workspace(int32_t total_nodes);
+// stochastic tree verification: workspace layout (byte offsets of the
+// per-node tables and share partials), a pure function of host scalars
+struct SampledLayout {
+  size_t node, child, step, part, bonus, total;
+  int C, S;  // children kept per node, shares per logits row
+};
+SampledLayout sampled_layout(int32_t total_nodes, int32_t max_children, int32_t vocab);
 hipError_t launch_accept_sampled(const int32_t* parent, const int32_t* draft_tok,
                                  const int32_t* cu_nodes, int32_t batch, int32_t total_nodes,
                                  int32_t max_nodes, int32_t max_children, int32_t max_depth,

@@ -12,106 +12,359 @@
 // accepted the bonus token is drawn from the current p by inverse transform
 // in token order.
 //
-// With the node's softmax values P(v) = 2^(c a_v - Lp), Q(v) = 2^(c b_v - Lq)
-// (a, b the target's and the draft's logits, c = log2(e) / T) and the tokens
-// x_0..x_{i-1} rejected so far:
-//   q_j(v) = Q(v) / M_j unless v is one of x_0..x_{j-1}, then 0
-//            (M_j = the draft mass left after j rejections, M_0 = 1);
-//   p_0 = P, p_{j+1}(v) = max(0, p_j(v) - q_j(v)) / Z_j
-//            (Z_j = sum_v max(0, p_j(v) - q_j(v)); p stays when Z_j = 0).
-// A child's test needs p_i and q_i at its token only; a rejection adds Z_i and
-// M_{i+1}, two sums over the vocabulary.
+// One parameter per step. With the node's softmax values P(v), Q(v) and the
+// draft mass M_r left after r rejections (M_0 = 1), every token not yet
+// rejected has
+//   p_r(v) = max(0, P(v) - beta_r Q(v)) / gamma_r,   q_r(v) = Q(v) / M_r,
+// with beta_0 = 0, gamma_0 = 1 and, writing F(beta) = sum_v max(0, P(v) -
+// beta Q(v)),
+//   beta_{r+1} = beta_r + gamma_r / M_r,   gamma_{r+1} = F(beta_{r+1})
+// (by induction: subtracting q_r from p_r and renormalising shifts beta and
+// rescales). A rejected token has q = 0 from then on and its residual is
+// already 0 (it was rejected because p <= u q < q), so F can sum over every
+// token. When F(beta_{r+1}) = 0 the residual is empty and p stays (beta,
+// gamma kept); when M_r = 0, q is zero and p stays too. So a node's whole
+// chain is a few evaluations of F, each a sum over the vocabulary, and the
+// bonus distribution after m rejections is max(0, P - beta_m Q) / gamma_m.
 //
-// sampled_norm_kernel: one 512-thread workgroup per node: Lp and Lq (NaN
-//   logits count as -inf), into the caller's workspace.
-// sampled_walk_kernel: one 1024-thread workgroup per request walks its tree
-//   from the root. The request's parent array sits in LDS; at each node the
-//   children are gathered in index order, their tokens, uniforms and the two
-//   logits at those tokens are read in parallel, and the children are tried
-//   with scalar arithmetic that every thread repeats. A rejection costs one
-//   pass over the node's two logit rows; the bonus costs one pass (per-thread
-//   runs of tokens in order, a block scan, then a rescan of the one run that
-//   holds the draw).
+// Kernels (every node of the batch in parallel; each node's rows are cut into
+// S shares, one 256-thread workgroup each):
+//   round 0:  share partials of both softmax normalisers; share 0 also lists
+//             the node's children (index order, tokens in the vocabulary)
+//             with their uniforms.
+//   round k:  (k = 1 .. max_children + 1) combine the shares' partials of the
+//             round before and fix (beta_{k-1}, gamma_{k-1}); then, for a node
+//             with m children, k <= m: share partials of F(beta_k) (round 1
+//             also the draft mass outside the children's tokens); k = m + 1:
+//             share sums of the bonus distribution.
+//   walk:     one 1024-thread workgroup per request: at each node one parallel
+//             read of its children and steps, the tests in order with scalar
+//             arithmetic every thread repeats, and for the bonus a scan of the
+//             share sums and an inverse transform inside the one share that
+//             holds the draw (per-thread runs in token order, a block scan,
+//             then a rescan of the one run).
+#include "tv_launch.h"
 #include "tv_vocab.h"
 
 namespace tv {
 namespace {
 
-constexpr int kNormThreads = 512;
-constexpr int kNormUnroll = 4;
+constexpr int kRoundThreads = 256;
+constexpr int kRoundWaves = kRoundThreads / 64;
+constexpr int kRoundUnroll = 8;  // units per thread in flight (a share is one sweep at 16,384 tokens)
 constexpr int kWalkThreads = 1024;
 constexpr int kWalkWaves = kWalkThreads / 64;
+constexpr int kMaxShares = 32;
 constexpr float kLog2eS = 1.4426950408889634f;
 
-__device__ __forceinline__ float nan_to_ninf(float x) { return (x == x) ? x : -INFINITY; }
+struct NodeInfo {
+  float lp, lq;  // log2 normalisers: P(v) = 2^(c a_v - lp), Q(v) = 2^(c b_v - lq)
+  float snc;     // draft mass outside the children's tokens
+  int32_t m;     // children kept (tokens in the vocabulary), at most max_children
+};
+struct ChildInfo {
+  int32_t tok, local;  // token, request-local node index
+  float P, Q, u;       // target / draft probability of the token, the child's uniform
+  int32_t dup;         // earlier child with the same token, or -1
+  int32_t pad[2];
+};
+struct Step {
+  float beta, gamma;
+};
 
-template <typename T, bool VEC>
-__global__ __launch_bounds__(kNormThreads) void sampled_norm_kernel(const T* __restrict__ tl,
-                                                                    const T* __restrict__ dl,
-                                                                    int64_t vocab, float c,
-                                                                    float2* __restrict__ norm) {
-  constexpr int W = VocabUnit<T, VEC>::W;
-  __shared__ MaxSum s_ms[kNormThreads / 64];
-  const int64_t node = blockIdx.x;
-  const T* a = tl + node * vocab;
-  const T* b = dl + node * vocab;
-  const int64_t units = vocab / W;  // VEC only when vocab % W == 0
-  MaxSum ra{-INFINITY, 0.f}, rb{-INFINITY, 0.f};
-  int64_t j = threadIdx.x;
-  for (; j + (kNormUnroll - 1) * kNormThreads < units; j += kNormUnroll * kNormThreads) {
-    float ya[kNormUnroll][W], yb[kNormUnroll][W];
-#pragma unroll
-    for (int u = 0; u < kNormUnroll; ++u) {
-      VocabUnit<T, VEC>::load(a + (j + u * kNormThreads) * W, ya[u]);
-      VocabUnit<T, VEC>::load(b + (j + u * kNormThreads) * W, yb[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < kNormUnroll; ++u) {
-#pragma unroll
-      for (int e = 0; e < W; ++e) {
-        ya[u][e] = nan_to_ninf(ya[u][e]);
-        yb[u][e] = nan_to_ninf(yb[u][e]);
-      }
-      fold(ra, ya[u], c);
-      fold(rb, yb[u], c);
-    }
-  }
-  for (; j < units; j += kNormThreads) {
-    float ya[W], yb[W];
-    VocabUnit<T, VEC>::load(a + j * W, ya);
-    VocabUnit<T, VEC>::load(b + j * W, yb);
-#pragma unroll
-    for (int e = 0; e < W; ++e) {
-      ya[e] = nan_to_ninf(ya[e]);
-      yb[e] = nan_to_ninf(yb[e]);
-    }
-    fold(ra, ya, c);
-    fold(rb, yb, c);
-  }
-  ra = block_merge<kNormThreads / 64>(ra, s_ms);
-  rb = block_merge<kNormThreads / 64>(rb, s_ms);
-  if (threadIdx.x == 0) norm[node] = make_float2(ra.m + __log2f(ra.s), rb.m + __log2f(rb.s));
-}
-
-struct WalkArgs {
+struct SArgs {
   const int32_t* parent;
   const int32_t* draft_tok;
   const int32_t* cu_nodes;
-  int32_t total_nodes, max_nodes, max_children, max_depth;
-  int64_t vocab;
-  float c;
   const float* u_accept;
   const float* u_bonus;
-  const float2* norm;
+  int32_t batch, total_nodes, max_nodes, max_depth;
+  int32_t C, S;  // children kept per node, shares per row
+  int64_t vocab;
+  float c;
+  NodeInfo* node;    // [N]
+  ChildInfo* child;  // [N][C]
+  Step* step;        // [N][C + 1]
+  float4* part;      // [2][N][S] share partials, by round parity
+  float* bonus;      // [N][S] share sums of the bonus distribution
   int32_t* accept_len;
   int32_t* path;
   int32_t* bonus_tok;
 };
 
-// Inclusive prefix sum over the block of one value per thread, in thread
-// order; s_w holds kWalkWaves floats. Returns the thread's inclusive sum and
-// the block total.
-__device__ float block_inclusive_sum(float v, float* s_w, float& total) {
+__device__ __forceinline__ float nan_to_ninf(float x) { return (x == x) ? x : -INFINITY; }
+// softmax value 2^(c x - L); a NaN logit gives 0 (max returns its non-NaN operand)
+__device__ __forceinline__ float prob(float x, float c, float L) {
+  return fmaxf(__builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -L)), 0.f);
+}
+
+// 1 / (draft mass left after the first r children are rejected): the mass
+// outside every child's token plus each remaining distinct token's; 1 for
+// r = 0 and 0 when nothing is left.
+__device__ float inv_mass(float snc, const ChildInfo* ch, int m, int r) {
+  if (r == 0) return 1.f;
+  float M = snc;
+  for (int j = r; j < m; ++j)
+    if (ch[j].dup < 0) M += ch[j].Q;
+  return M > 0.f ? 1.f / M : 0.f;
+}
+
+// Share s of a row of `units` units: [u0, u1).
+__device__ __forceinline__ void share(int64_t units, int S, int s, int64_t& u0, int64_t& u1) {
+  const int64_t per = (units + S - 1) / S;
+  u0 = min(units, (int64_t)s * per);
+  u1 = min(units, u0 + per);
+}
+
+// Visit the units [u0, u1) of two rows, kRoundUnroll units per thread in
+// flight at once (loads from a clamped index, so that a thread's loads are
+// issued together); fn(ya, yb, unit, valid).
+template <typename T, bool VEC, typename Fn>
+__device__ __forceinline__ void for_units(const T* ra, const T* rb, int64_t u0, int64_t u1, Fn&& fn) {
+  constexpr int W = VocabUnit<T, VEC>::W;
+  for (int64_t base = u0; base < u1; base += kRoundUnroll * kRoundThreads) {
+    float ya[kRoundUnroll][W], yb[kRoundUnroll][W];
+#pragma unroll
+    for (int u = 0; u < kRoundUnroll; ++u) {
+      const int64_t j = min(base + u * kRoundThreads + (int64_t)threadIdx.x, u1 - 1);
+      VocabUnit<T, VEC>::load(ra + j * W, ya[u]);
+      VocabUnit<T, VEC>::load(rb + j * W, yb[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kRoundUnroll; ++u) {
+      const int64_t j = base + u * kRoundThreads + threadIdx.x;
+      fn(ya[u], yb[u], j, j < u1);
+    }
+  }
+}
+
+// Sum over a round workgroup of two values per thread.
+__device__ float2 round_sum2(float x, float y, float2* s_red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    x += __shfl_xor(x, off, 64);
+    y += __shfl_xor(y, off, 64);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) s_red[wave] = make_float2(x, y);
+  __syncthreads();
+  float2 r = s_red[0];
+#pragma unroll
+  for (int w = 1; w < kRoundWaves; ++w) {
+    r.x += s_red[w].x;
+    r.y += s_red[w].y;
+  }
+  __syncthreads();
+  return r;
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kRoundThreads) void sampled_round0_kernel(SArgs a, const T* __restrict__ tl,
+                                                                       const T* __restrict__ dl) {
+  constexpr int W = VocabUnit<T, VEC>::W;
+  __shared__ MaxSum s_ms[kRoundWaves];
+  __shared__ int s_cnt[kRoundWaves];
+  const int g = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t units = a.vocab / W;  // VEC only when vocab % W == 0
+  int64_t u0, u1;
+  share(units, a.S, s, u0, u1);
+  const T* ra = tl + (int64_t)g * a.vocab;
+  const T* rb = dl + (int64_t)g * a.vocab;
+  MaxSum mp{-INFINITY, 0.f}, mq{-INFINITY, 0.f};
+  for_units<T, VEC>(ra, rb, u0, u1, [&](float (&ya)[W], float (&yb)[W], int64_t, bool valid) {
+    if (!valid) return;
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+      ya[e] = nan_to_ninf(ya[e]);
+      yb[e] = nan_to_ninf(yb[e]);
+    }
+    fold(mp, ya, a.c);
+    fold(mq, yb, a.c);
+  });
+  mp = block_merge<kRoundWaves>(mp, s_ms);
+  mq = block_merge<kRoundWaves>(mq, s_ms);
+  if (tid == 0) a.part[(size_t)g * a.S + s] = make_float4(mp.m, mp.s, mq.m, mq.s);
+  if (s != 0) return;
+
+  // the node's request (cu_nodes ascending: cu[b] <= g < cu[b + 1]) and its
+  // children in index order
+  int lo = 0, hi = a.batch;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu_nodes[mid] <= g) lo = mid;
+    else hi = mid;
+  }
+  const int r0 = clampi(a.cu_nodes[lo], 0, a.total_nodes);
+  const int r1 = clampi(a.cu_nodes[lo + 1], r0, a.total_nodes);
+  const int n = min(r1 - r0, a.max_nodes);
+  const int local = g - r0;
+  int m = 0;
+  if (local >= 0 && local < n) {  // (uniform; false only for malformed offsets)
+    ChildInfo* ch = a.child + (size_t)g * a.C;
+    for (int base = local + 1; base < n; base += kRoundThreads) {
+      const int ci = base + tid;
+      int x = -1;
+      bool is = false;
+      if (ci < n && a.parent[r0 + ci] == local) {
+        x = a.draft_tok[r0 + ci];
+        is = x >= 0 && (int64_t)x < a.vocab;  // a token outside the vocabulary is passed over
+      }
+      const uint64_t bal = __ballot(is);
+      if (lane == 0) s_cnt[wave] = __popcll(bal);
+      __syncthreads();
+      int off = m, tot = 0;
+#pragma unroll
+      for (int w = 0; w < kRoundWaves; ++w) {
+        const int cnt = s_cnt[w];
+        off += (w < wave) ? cnt : 0;
+        tot += cnt;
+      }
+      const int pos = off + __popcll(bal & ((1ull << lane) - 1));
+      if (is && pos < a.C) {
+        ChildInfo c{};
+        c.tok = x;
+        c.local = ci;
+        c.u = a.u_accept[r0 + ci];
+        c.dup = -1;
+        ch[pos] = c;
+      }
+      m += tot;
+      __syncthreads();
+    }
+  }
+  if (tid == 0) {
+    NodeInfo ni{};
+    ni.m = min(m, a.C);
+    a.node[g] = ni;
+  }
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kRoundThreads) void sampled_round_kernel(SArgs a, int k,
+                                                                      const T* __restrict__ tl,
+                                                                      const T* __restrict__ dl) {
+  constexpr int W = VocabUnit<T, VEC>::W;
+  __shared__ float2 s_red[kRoundWaves];
+  __shared__ ChildInfo s_ch[TV_MAX_SAMPLED_CHILDREN];
+  const int g = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+  const bool lead = (s == 0 && tid == 0);
+  NodeInfo ni = a.node[g];
+  const int m = ni.m;
+  if (k > m + 1) return;  // this node's chain and bonus are done (uniform)
+  const int S = a.S;
+  const float4* prev = a.part + (size_t)((k - 1) & 1) * a.total_nodes * S + (size_t)g * S;
+  ChildInfo* ch = a.child + (size_t)g * a.C;
+  Step* st = a.step + (size_t)g * (a.C + 1);
+  const T* ra = tl + (int64_t)g * a.vocab;
+  const T* rb = dl + (int64_t)g * a.vocab;
+
+  if (k == 1) {
+    // normalisers from the shares, in share order (every workgroup alike)
+    MaxSum mp{-INFINITY, 0.f}, mq{-INFINITY, 0.f};
+    for (int i = 0; i < S; ++i) {
+      const float4 p = prev[i];
+      mp = merge(mp, MaxSum{p.x, p.y});
+      mq = merge(mq, MaxSum{p.z, p.w});
+    }
+    ni.lp = mp.m + __log2f(mp.s);
+    ni.lq = mq.m + __log2f(mq.s);
+  } else if (k == 2) {
+    float snc = 0.f;
+    for (int i = 0; i < S; ++i) snc += prev[i].y;
+    ni.snc = snc;
+  }
+  // the children: round 1 fills in the probabilities of their tokens and the
+  // repeated tokens, later rounds read them
+  for (int j = tid; j < m; j += kRoundThreads) {
+    ChildInfo c = ch[j];
+    if (k == 1) {
+      c.P = prob(load_one(ra + c.tok), a.c, ni.lp);
+      c.Q = prob(load_one(rb + c.tok), a.c, ni.lq);
+      c.dup = -1;
+      for (int i = 0; i < j; ++i)
+        if (ch[i].tok == c.tok) {
+          c.dup = i;
+          break;
+        }
+    }
+    s_ch[j] = c;
+  }
+  __syncthreads();
+  if (s == 0 && k == 1)
+    for (int j = tid; j < m; j += kRoundThreads) ch[j] = s_ch[j];
+  if (lead && k <= 2) a.node[g] = ni;
+
+  // (beta_{k-1}, gamma_{k-1})
+  Step cur{0.f, 1.f};
+  if (k >= 2) {
+    const Step pk = st[k - 2];
+    const float beta = pk.beta + pk.gamma * inv_mass(ni.snc, s_ch, m, k - 2);
+    float F = 0.f;
+    for (int i = 0; i < S; ++i) F += prev[i].x;
+    cur = (F > 0.f) ? Step{beta, F} : pk;
+  }
+  if (lead) st[k - 1] = cur;
+
+  const int64_t units = a.vocab / W;
+  int64_t u0, u1;
+  share(units, S, s, u0, u1);
+  if (k <= m) {
+    // share partial of F(beta_k); round 1 also the draft mass outside the children
+    const float beta = cur.beta + cur.gamma * inv_mass(ni.snc, s_ch, m, k - 1);
+    float f = 0.f, snc = 0.f;
+    for_units<T, VEC>(ra, rb, u0, u1, [&](float (&ya)[W], float (&yb)[W], int64_t j, bool valid) {
+      if (!valid) return;
+      float Q[W];
+#pragma unroll
+      for (int e = 0; e < W; ++e) {
+        const float P = prob(ya[e], a.c, ni.lp);
+        Q[e] = prob(yb[e], a.c, ni.lq);
+        f += fmaxf(0.f, __builtin_fmaf(-beta, Q[e], P));
+      }
+      if (k == 1) {
+        // draft mass outside the children's tokens: a unit holding none of
+        // them adds all its values, else value by value
+        bool hit = false;
+        for (int i = 0; i < m; ++i) hit |= (s_ch[i].tok / W == j);
+        if (!hit) {
+#pragma unroll
+          for (int e = 0; e < W; ++e) snc += Q[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < W; ++e) {
+            const int v = (int)(j * W + e);
+            bool child = false;
+            for (int i = 0; i < m; ++i) child |= (s_ch[i].tok == v);
+            snc += child ? 0.f : Q[e];
+          }
+        }
+      }
+    });
+    const float2 r = round_sum2(f, snc, s_red);
+    if (tid == 0)
+      a.part[(size_t)(k & 1) * a.total_nodes * S + (size_t)g * S + s] = make_float4(r.x, r.y, 0.f, 0.f);
+  } else {
+    // k = m + 1: share sum of the bonus distribution max(0, P - beta Q) / gamma
+    const float ig = 1.f / cur.gamma;
+    float sum = 0.f;
+    for_units<T, VEC>(ra, rb, u0, u1, [&](float (&ya)[W], float (&yb)[W], int64_t, bool valid) {
+      if (!valid) return;
+#pragma unroll
+      for (int e = 0; e < W; ++e) {
+        const float P = prob(ya[e], a.c, ni.lp);
+        const float Q = prob(yb[e], a.c, ni.lq);
+        sum += fmaxf(0.f, __builtin_fmaf(-cur.beta, Q, P)) * ig;
+      }
+    });
+    const float2 r = round_sum2(sum, 0.f, s_red);
+    if (tid == 0) a.bonus[(size_t)g * S + s] = r.x;
+  }
+}
+
+// Inclusive prefix sum over the walk block of one value per thread, in thread
+// order; returns the thread's inclusive sum and the block total.
+__device__ float walk_inclusive_sum(float v, float* s_w, float& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float x = v;
 #pragma unroll
@@ -133,251 +386,236 @@ __device__ float block_inclusive_sum(float v, float* s_w, float& total) {
   return before + x;
 }
 
+// Walk storage in dynamic LDS: K node slots of children [K][C], steps
+// [K][C + 1], node info [K] and share sums [K][S]. K = the request's node cap
+// when that fits (everything is read once, up front), else 1 (one node read
+// per level).
+__host__ __device__ inline size_t walk_slot_bytes(int C, int S) {
+  return (size_t)C * sizeof(ChildInfo) + (size_t)(C + 1) * sizeof(Step) + sizeof(NodeInfo) +
+         (size_t)S * sizeof(float);
+}
+constexpr size_t kWalkPreloadBytes = 48 * 1024;
+
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kWalkThreads) void sampled_walk_kernel(WalkArgs w,
+__global__ __launch_bounds__(kWalkThreads) void sampled_walk_kernel(SArgs a, int preload,
                                                                     const T* __restrict__ tl,
                                                                     const T* __restrict__ dl) {
   constexpr int W = VocabUnit<T, VEC>::W;
-  extern __shared__ int32_t s_dyn[];
-  const int cap = w.max_nodes, cc = w.max_children;
-  int32_t* s_par = s_dyn;                                 // [cap] request-local parents
-  int32_t* s_kid = s_par + cap;                           // [cc] children of the current node
-  int32_t* s_tok = s_kid + cc;                            // [cc] their tokens (-1: outside the vocabulary)
-  float* s_u = reinterpret_cast<float*>(s_tok + cc);      // [cc] their uniforms
-  float* s_a = s_u + cc;                                  // [cc] target logit at each token
-  float* s_b = s_a + cc;                                  // [cc] draft logit at each token
-  int32_t* s_rx = reinterpret_cast<int32_t*>(s_b + cc);   // [cc] rejected tokens, in order
-  float* s_iz = reinterpret_cast<float*>(s_rx + cc);      // [cc] 1 / Z_j (0: Z_j = 0)
-  float* s_im = s_iz + cc;                                // [cc + 1] 1 / M_j (0: no draft mass left)
-  __shared__ float s_red[2][kWalkWaves];
-  __shared__ int s_cnt[kWalkWaves];
-  __shared__ float s_incl[kWalkWaves];
+  extern __shared__ float4 s_dyn4[];
+  __shared__ float s_w[kWalkWaves], s_incl[kWalkWaves];
   __shared__ int s_pick, s_last;
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
-  const int lo = clampi(w.cu_nodes[b], 0, w.total_nodes);
-  const int hi = clampi(w.cu_nodes[b + 1], lo, w.total_nodes);
-  const int n = min(hi - lo, cap);
-  const int prow = w.max_depth + 1;
-  int32_t* path = w.path + (size_t)b * prow;
-  for (int i = tid; i < n; i += kWalkThreads) s_par[i] = w.parent[lo + i];
+  const int lo = clampi(a.cu_nodes[b], 0, a.total_nodes);
+  const int hi = clampi(a.cu_nodes[b + 1], lo, a.total_nodes);
+  const int n = min(hi - lo, a.max_nodes);
+  const int prow = a.max_depth + 1;
+  int32_t* path = a.path + (size_t)b * prow;
   for (int d = tid; d < prow; d += kWalkThreads) path[d] = (d == 0 && n > 0) ? 0 : -1;
-  if (n == 0) {  // an empty request (uniform over the block)
+  if (n == 0) {  // an empty request (uniform)
     if (tid == 0) {
-      w.accept_len[b] = 0;
-      w.bonus_tok[b] = -1;
+      a.accept_len[b] = 0;
+      a.bonus_tok[b] = -1;
     }
     return;
   }
-  __syncthreads();
-
-  // p_i(v) and q_i(v) after i rejections, from P(v), Q(v); `rej` = index of
-  // v's first rejection among 0..i-1, or i. Every thread gets the same values
-  // for the same inputs (LDS reads only).
-  auto chain = [&](int v, float P, float Q, int i, float& p, float& q, int& rej) {
-    rej = i;
-    for (int l = 0; l < i; ++l)
-      if (s_rx[l] == v) {
-        rej = l;
-        break;
-      }
-    p = P;
-    for (int j = 0; j < i; ++j) {
-      const float qj = (rej < j) ? 0.f : Q * s_im[j];
-      const float iz = s_iz[j];
-      p = (iz > 0.f) ? fmaxf(0.f, p - qj) * iz : p;
-    }
-    q = (rej < i) ? 0.f : Q * s_im[i];
+  const int C = a.C, S = a.S;
+  const int K = preload ? a.max_nodes : 1;
+  ChildInfo* s_chs = reinterpret_cast<ChildInfo*>(s_dyn4);
+  Step* s_sts = reinterpret_cast<Step*>(s_chs + (size_t)K * C);
+  NodeInfo* s_nis = reinterpret_cast<NodeInfo*>(s_sts + (size_t)K * (C + 1));
+  float* s_shs = reinterpret_cast<float*>(s_nis + K);
+  // copy nodes [first, first + cnt) of the request into slots [0, cnt)
+  auto fetch = [&](int first, int cnt) {
+    const size_t g0 = (size_t)lo + first;
+    for (int i = tid; i < cnt * C; i += kWalkThreads) s_chs[i] = a.child[g0 * C + i];
+    for (int i = tid; i < cnt * (C + 1); i += kWalkThreads) s_sts[i] = a.step[g0 * (C + 1) + i];
+    for (int i = tid; i < cnt; i += kWalkThreads) s_nis[i] = a.node[g0 + i];
+    for (int i = tid; i < cnt * S; i += kWalkThreads) s_shs[i] = a.bonus[g0 * S + i];
   };
-  const int64_t units = w.vocab / W;
+  if (preload) fetch(0, n);
+  __syncthreads();
+  const int64_t units = a.vocab / W;
 
   int node = 0, depth = 0;
   for (;;) {
-    const float2 L = w.norm[lo + node];
-    const int64_t row = (int64_t)(lo + node) * w.vocab;
-    // children of `node`, in index order (the first cc of them)
-    int m = 0;
-    for (int base = node + 1; base < n; base += kWalkThreads) {
-      const int ci = base + tid;
-      const bool is = ci < n && s_par[ci] == node;
-      const uint64_t bal = __ballot(is);
-      if (lane == 0) s_cnt[wave] = __popcll(bal);
-      __syncthreads();
-      int off = m, tot = 0;
-#pragma unroll
-      for (int x = 0; x < kWalkWaves; ++x) {
-        const int cnt = s_cnt[x];
-        off += (x < wave) ? cnt : 0;
-        tot += cnt;
-      }
-      const int pos = off + __popcll(bal & ((1ull << lane) - 1));
-      if (is && pos < cc) s_kid[pos] = ci;
-      m += tot;
+    const int g = lo + node;
+    if (!preload) {  // one round trip for the node, all its slots
+      fetch(node, 1);
       __syncthreads();
     }
-    m = min(m, cc);
-    for (int k = tid; k < m; k += kWalkThreads) {
-      const int g = lo + s_kid[k];
-      const int x = w.draft_tok[g];
-      const bool ok = x >= 0 && (int64_t)x < w.vocab;
-      s_tok[k] = ok ? x : -1;
-      s_u[k] = w.u_accept[g];
-      s_a[k] = ok ? nan_to_ninf(load_one(tl + row + x)) : -INFINITY;
-      s_b[k] = ok ? nan_to_ninf(load_one(dl + row + x)) : -INFINITY;
-    }
-    if (tid == 0) s_im[0] = 1.f;
-    __syncthreads();
-
-    // try the children in order
-    int i = 0, next = -1;
-    for (int k = 0; k < m; ++k) {
-      const int x = s_tok[k];
-      if (x < 0) continue;  // not a token of the vocabulary: passed over
-      const float P = __builtin_amdgcn_exp2f(__builtin_fmaf(s_a[k], w.c, -L.x));
-      const float Q = __builtin_amdgcn_exp2f(__builtin_fmaf(s_b[k], w.c, -L.y));
+    const int slot = preload ? node : 0;
+    const ChildInfo* s_ch = s_chs + (size_t)slot * C;
+    const Step* s_st = s_sts + (size_t)slot * (C + 1);
+    const float* s_share = s_shs + (size_t)slot * S;
+    const NodeInfo ni = s_nis[slot];
+    const int m = ni.m;
+    // the children in order (every thread takes the same decisions)
+    int next = -1;
+    for (int l = 0; l < m; ++l) {
+      const ChildInfo c = s_ch[l];
       float p, q;
-      int rej;
-      chain(x, P, Q, i, p, q, rej);
-      if (s_u[k] * q < p) {
-        next = s_kid[k];
+      if (c.dup >= 0) {  // its token was rejected before: q is 0, the residual frozen
+        q = 0.f;
+        p = fmaxf(0.f, __builtin_fmaf(-s_st[c.dup + 1].beta, c.Q, c.P)) / s_st[l].gamma;
+      } else {
+        q = c.Q * inv_mass(ni.snc, s_ch, m, l);
+        p = fmaxf(0.f, __builtin_fmaf(-s_st[l].beta, c.Q, c.P)) / s_st[l].gamma;
+      }
+      if (c.u * q < p) {
+        next = c.local;
         break;
       }
-      // rejected: Z_i and M_{i+1} over the vocabulary
-      if (tid == 0) s_rx[i] = x;
-      __syncthreads();
-      float zs = 0.f, ms = 0.f;
-      for (int64_t j = tid; j < units; j += kWalkThreads) {
-        float ya[W], yb[W];
-        VocabUnit<T, VEC>::load(tl + row + j * W, ya);
-        VocabUnit<T, VEC>::load(dl + row + j * W, yb);
-#pragma unroll
-        for (int e = 0; e < W; ++e) {
-          const int v = (int)(j * W + e);
-          const float Pv = __builtin_amdgcn_exp2f(__builtin_fmaf(nan_to_ninf(ya[e]), w.c, -L.x));
-          const float Qv = __builtin_amdgcn_exp2f(__builtin_fmaf(nan_to_ninf(yb[e]), w.c, -L.y));
-          float pv, qv;
-          int rv;
-          chain(v, Pv, Qv, i, pv, qv, rv);
-          zs += fmaxf(0.f, pv - qv);
-          ms += (rv == i && v != x) ? Qv : 0.f;
-        }
-      }
-      zs = block_sum<kWalkWaves>(zs, s_red[0]);
-      ms = block_sum<kWalkWaves>(ms, s_red[1]);
-      if (tid == 0) {
-        s_iz[i] = zs > 0.f ? 1.f / zs : 0.f;
-        s_im[i + 1] = ms > 0.f ? 1.f / ms : 0.f;
-      }
-      __syncthreads();
-      ++i;
     }
-
-    if (next >= 0) {
+    if (next > node && next < n) {
       node = next;
       ++depth;
-      if (tid == 0 && depth <= w.max_depth) path[depth] = node;
+      if (tid == 0 && depth <= a.max_depth) path[depth] = node;
+      if (!preload) __syncthreads();  // slot 0 is refilled for the next node
       continue;
     }
 
-    // bonus token: inverse transform of p_i in token order
-    const int64_t per = (units + kWalkThreads - 1) / kWalkThreads;
-    const int64_t j0 = min(units, (int64_t)tid * per), j1 = min(units, j0 + per);
-    auto p_at = [&](int64_t j, float (&pv)[W]) {
-      float ya[W], yb[W];
-      VocabUnit<T, VEC>::load(tl + row + j * W, ya);
-      VocabUnit<T, VEC>::load(dl + row + j * W, yb);
-#pragma unroll
-      for (int e = 0; e < W; ++e) {
-        const float Pv = __builtin_amdgcn_exp2f(__builtin_fmaf(nan_to_ninf(ya[e]), w.c, -L.x));
-        const float Qv = __builtin_amdgcn_exp2f(__builtin_fmaf(nan_to_ninf(yb[e]), w.c, -L.y));
-        float qv;
-        int rv;
-        chain((int)(j * W + e), Pv, Qv, i, pv[e], qv, rv);
+    // bonus: the share that holds the draw, then inverse transform inside it
+    const Step fin = s_st[m];
+    const float ig = 1.f / fin.gamma;
+    float total = 0.f;
+    for (int i = 0; i < S; ++i) total += s_share[i];
+    const float target = a.u_bonus[b] * total;
+    int sh = -1, last_sh = -1;
+    float before = 0.f, acc = 0.f;
+    for (int i = 0; i < S; ++i) {
+      const float nx = acc + s_share[i];
+      if (s_share[i] > 0.f) last_sh = i;
+      if (sh < 0 && acc <= target && target < nx) {
+        sh = i;
+        before = acc;
       }
-    };
-    float s = 0.f;
-    for (int64_t j = j0; j < j1; ++j) {
-      float pv[W];
-      p_at(j, pv);
-#pragma unroll
-      for (int e = 0; e < W; ++e) s += pv[e];
+      acc = nx;
     }
-    float total;
-    const float incl = block_inclusive_sum(s, s_red[0], total);
-    // the previous thread's inclusive sum: a shuffle within the wave, LDS
-    // across waves, so the runs [excl, incl) tile [0, total) exactly
-    if (lane == 63) s_incl[wave] = incl;
-    if (tid == 0) {
-      s_pick = -1;
-      s_last = -1;
-    }
-    __syncthreads();
-    float excl = __shfl_up(incl, 1, 64);
-    if (lane == 0) excl = (wave == 0) ? 0.f : s_incl[wave - 1];
-    const float target = w.u_bonus[b] * total;
-    // exactly one run holds the draw unless rounding put it at or past the
-    // total
-    if (excl <= target && target < incl) {
-      float r = excl;
-      int pick = -1, last = -1;
-      for (int64_t j = j0; j < j1 && pick < 0; ++j) {
-        float pv[W];
-        p_at(j, pv);
+    const bool past = sh < 0;  // at or past the total: the last token with mass
+    if (past) sh = last_sh;
+    int pick = -1;
+    if (sh >= 0) {
+      int64_t u0, u1;
+      share(units, S, sh, u0, u1);
+      const int64_t per = (u1 - u0 + kWalkThreads - 1) / kWalkThreads;
+      const int64_t j0 = min(u1, u0 + (int64_t)tid * per), j1 = min(u1, j0 + per);
+      const T* ra = tl + (int64_t)g * a.vocab;
+      const T* rb = dl + (int64_t)g * a.vocab;
+      auto p_at = [&](int64_t j, float (&pv)[W]) {
+        float ya[W], yb[W];
+        VocabUnit<T, VEC>::load(ra + j * W, ya);
+        VocabUnit<T, VEC>::load(rb + j * W, yb);
 #pragma unroll
         for (int e = 0; e < W; ++e) {
-          if (pick >= 0) break;
-          if (pv[e] > 0.f) last = (int)(j * W + e);
-          r += pv[e];
-          if (r > target && pv[e] > 0.f) pick = (int)(j * W + e);
+          const float P = prob(ya[e], a.c, ni.lp);
+          const float Q = prob(yb[e], a.c, ni.lq);
+          pv[e] = fmaxf(0.f, __builtin_fmaf(-fin.beta, Q, P)) * ig;
         }
-      }
-      s_pick = pick >= 0 ? pick : last;
-    }
-    if (s > 0.f) atomicMax(&s_last, tid);
-    __syncthreads();
-    if (s_pick < 0 && tid == s_last) {
-      // the draw fell at or past the total: the last token with mass
-      int last = -1;
+      };
+      float run = 0.f;
       for (int64_t j = j0; j < j1; ++j) {
         float pv[W];
         p_at(j, pv);
 #pragma unroll
-        for (int e = 0; e < W; ++e)
-          if (pv[e] > 0.f) last = (int)(j * W + e);
+        for (int e = 0; e < W; ++e) run += pv[e];
       }
-      s_pick = last;
+      float stotal;
+      const float incl = walk_inclusive_sum(run, s_w, stotal);
+      // the previous thread's inclusive sum: a shuffle within the wave, LDS
+      // across waves, so the runs [excl, incl) tile [0, stotal) exactly
+      if (lane == 63) s_incl[wave] = incl;
+      if (tid == 0) {
+        s_pick = -1;
+        s_last = -1;
+      }
+      __syncthreads();
+      float excl = __shfl_up(incl, 1, 64);
+      if (lane == 0) excl = (wave == 0) ? 0.f : s_incl[wave - 1];
+      const float t = past ? INFINITY : target - before;
+      if (excl <= t && t < incl) {
+        float r = excl;
+        int pk = -1, last = -1;
+        for (int64_t j = j0; j < j1 && pk < 0; ++j) {
+          float pv[W];
+          p_at(j, pv);
+#pragma unroll
+          for (int e = 0; e < W; ++e) {
+            if (pk >= 0) break;
+            if (pv[e] > 0.f) last = (int)(j * W + e);
+            r += pv[e];
+            if (r > t && pv[e] > 0.f) pk = (int)(j * W + e);
+          }
+        }
+        s_pick = pk >= 0 ? pk : last;
+      }
+      if (run > 0.f) atomicMax(&s_last, tid);
+      __syncthreads();
+      if (s_pick < 0 && tid == s_last) {
+        // rounding left the draw outside every run: the last token with mass
+        int last = -1;
+        for (int64_t j = j0; j < j1; ++j) {
+          float pv[W];
+          p_at(j, pv);
+#pragma unroll
+          for (int e = 0; e < W; ++e)
+            if (pv[e] > 0.f) last = (int)(j * W + e);
+        }
+        s_pick = last;
+      }
+      __syncthreads();
+      pick = s_pick;
     }
-    __syncthreads();
     if (tid == 0) {
-      w.bonus_tok[b] = s_pick;
-      w.accept_len[b] = depth;
+      a.bonus_tok[b] = pick;
+      a.accept_len[b] = depth;
     }
     return;
   }
 }
 
 template <typename T, bool VEC>
-hipError_t run_sampled(const WalkArgs& a, const void* tl, const void* dl, int32_t batch,
-                       int32_t total_nodes, float c, hipStream_t stream) {
+hipError_t run_sampled(const SArgs& a, const void* tl, const void* dl, hipStream_t stream) {
   const T* t = static_cast<const T*>(tl);
   const T* d = static_cast<const T*>(dl);
-  if (total_nodes > 0)
-    hipLaunchKernelGGL((sampled_norm_kernel<T, VEC>), dim3(total_nodes), dim3(kNormThreads), 0,
-                       stream, t, d, a.vocab, c, const_cast<float2*>(a.norm));
-  if (batch > 0) {
-    // s_par [max_nodes], seven per-child arrays [max_children] and s_im [max_children + 1]
-    const size_t lds = ((size_t)a.max_nodes + (size_t)8 * a.max_children + 1) * 4;
-    hipLaunchKernelGGL((sampled_walk_kernel<T, VEC>), dim3(batch), dim3(kWalkThreads), lds, stream,
-                       a, t, d);
+  if (a.total_nodes > 0) {
+    const dim3 grid(a.total_nodes, a.S);
+    hipLaunchKernelGGL((sampled_round0_kernel<T, VEC>), grid, dim3(kRoundThreads), 0, stream, a, t, d);
+    for (int k = 1; k <= a.C + 1; ++k)
+      hipLaunchKernelGGL((sampled_round_kernel<T, VEC>), grid, dim3(kRoundThreads), 0, stream, a, k,
+                         t, d);
   }
+  const size_t slot = walk_slot_bytes(a.C, a.S);
+  const int preload = (size_t)a.max_nodes * slot <= kWalkPreloadBytes ? 1 : 0;
+  const size_t lds = (preload ? (size_t)a.max_nodes : 1) * slot;
+  hipLaunchKernelGGL((sampled_walk_kernel<T, VEC>), dim3(a.batch), dim3(kWalkThreads), lds, stream, a,
+                     preload, t, d);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t sampled_workspace(int32_t total_nodes) {
-  return ((size_t)total_nodes * sizeof(float2) + 255) / 256 * 256;
+SampledLayout sampled_layout(int32_t total_nodes, int32_t max_children, int32_t vocab) {
+  SampledLayout L{};
+  L.C = max_children < 1 ? 1 : max_children;
+  // shares per row: about four workgroups per CU over the batch's rows, at
+  // least 16,384 tokens a share
+  const int64_t nodes = total_nodes > 0 ? total_nodes : 1;
+  int64_t s = (4 * 256 + nodes - 1) / nodes;
+  const int64_t by_len = ((int64_t)vocab + 16383) / 16384;
+  if (s > by_len) s = by_len;
+  if (s > kMaxShares) s = kMaxShares;
+  if (s < 1) s = 1;
+  L.S = (int)s;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t N = total_nodes > 0 ? (size_t)total_nodes : 0;
+  L.node = 0;
+  L.child = L.node + up(N * sizeof(NodeInfo));
+  L.step = L.child + up(N * L.C * sizeof(ChildInfo));
+  L.part = L.step + up(N * (L.C + 1) * sizeof(Step));
+  L.bonus = L.part + up(2 * N * L.S * sizeof(float4));
+  L.total = L.bonus + up(N * L.S * sizeof(float));
+  return L;
 }
 
 hipError_t launch_accept_sampled(const int32_t* parent, const int32_t* draft_tok,
@@ -388,30 +626,38 @@ hipError_t launch_accept_sampled(const int32_t* parent, const int32_t* draft_tok
                                  const float* u_accept, const float* u_bonus,
                                  int32_t* accept_len, int32_t* path, int32_t* bonus_tok,
                                  void* workspace, hipStream_t stream) {
-  WalkArgs a;
+  const SampledLayout L = sampled_layout(total_nodes, max_children, vocab);
+  char* ws = static_cast<char*>(workspace);
+  SArgs a;
   a.parent = parent;
   a.draft_tok = draft_tok;
   a.cu_nodes = cu_nodes;
-  a.total_nodes = total_nodes;
-  a.max_nodes = max_nodes;
-  a.max_children = max_children < 1 ? 1 : max_children;
-  a.max_depth = max_depth;
-  a.vocab = vocab;
-  a.c = kLog2eS / temperature;
   a.u_accept = u_accept;
   a.u_bonus = u_bonus;
-  a.norm = static_cast<const float2*>(workspace);
+  a.batch = batch;
+  a.total_nodes = total_nodes;
+  a.max_nodes = max_nodes;
+  a.max_depth = max_depth;
+  a.C = L.C;
+  a.S = L.S;
+  a.vocab = vocab;
+  a.c = kLog2eS / temperature;
+  a.node = reinterpret_cast<NodeInfo*>(ws + L.node);
+  a.child = reinterpret_cast<ChildInfo*>(ws + L.child);
+  a.step = reinterpret_cast<Step*>(ws + L.step);
+  a.part = reinterpret_cast<float4*>(ws + L.part);
+  a.bonus = reinterpret_cast<float*>(ws + L.bonus);
   a.accept_len = accept_len;
   a.path = path;
   a.bonus_tok = bonus_tok;
   if (dtype == TV_BF16) {
     const bool vec = vocab_vec<__bf16>(target_logits, vocab) && vocab_vec<__bf16>(draft_logits, vocab);
-    return vec ? run_sampled<__bf16, true>(a, target_logits, draft_logits, batch, total_nodes, a.c, stream)
-               : run_sampled<__bf16, false>(a, target_logits, draft_logits, batch, total_nodes, a.c, stream);
+    return vec ? run_sampled<__bf16, true>(a, target_logits, draft_logits, stream)
+               : run_sampled<__bf16, false>(a, target_logits, draft_logits, stream);
   }
   const bool vec = vocab_vec<float>(target_logits, vocab) && vocab_vec<float>(draft_logits, vocab);
-  return vec ? run_sampled<float, true>(a, target_logits, draft_logits, batch, total_nodes, a.c, stream)
-             : run_sampled<float, false>(a, target_logits, draft_logits, batch, total_nodes, a.c, stream);
+  return vec ? run_sampled<float, true>(a, target_logits, draft_logits, stream)
+             : run_sampled<float, false>(a, target_logits, draft_logits, stream);
 }
 
 }  // namespace tv
