@@ -302,7 +302,8 @@ def accept_sampled(parent, draft_tok, cu_nodes, target_logits, draft_logits, tem
     logits after node i (the draft's row is the distribution node i's
     children were drawn from); ``u_accept`` [N], ``u_bonus`` [B] in [0, 1).
     Returns (accept_len [B], path [B, max_depth+1] local ids root..last
-    accepted then -1, bonus [B], margin [B]); margin is the smallest distance
+    accepted then -1, bonus [B], margin [B]); an empty request gives 0, a
+    path of -1 and bonus -1. margin is the smallest distance
     of any decision from its boundary (|u q(x) - p(x)| for a child test, the
     distance of u_bonus * sum(p) to the nearest cumulative boundary for the
     bonus), so a test can tell a rounding-level tie from a disagreement.
@@ -323,6 +324,9 @@ def accept_sampled(parent, draft_tok, cu_nodes, target_logits, draft_logits, tem
     margin = np.full(batch, np.inf)
     for b in range(batch):
         lo, hi = int(cu[b]), int(cu[b + 1])
+        if hi <= lo:                             # an empty request: nothing to verify
+            bonus[b] = -1
+            continue
         node, depth = 0, 0
         path[b, 0] = 0
         while True:
