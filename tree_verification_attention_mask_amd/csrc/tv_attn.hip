@@ -65,7 +65,7 @@ struct Params {
   MaskDev mask;
   __bf16* out;
   float* lse;
-  float* part_o;   // [splits][total_nodes*hq][D]
+  __bf16* part_o;  // [splits][total_nodes*hq][D] the split's output over its own l
   float* part_ml;  // [splits][total_nodes*hq][2]  (m in log2 units, l)
   int32_t num_pages, max_pages, batch, total_nodes;
   int32_t hq, hkv, group, page_size;
@@ -739,10 +739,17 @@ void attn_bf16_kernel(Params p) {
       if (p.lse && q4 == 0)
         p.lse[orow[r]] = l_run[r] > 0.f ? (m_run[r] + log2f(l_run[r])) * kLn2 : -INFINITY;
     } else {
+      // the split's own softmax average in bf16 (the merge weights it by l):
+      // half the bytes of the raw fp32 sums, one more rounding of O
       const size_t prow = (size_t)split * R_tot + orow[r];
+      const float inv = l_run[r] > 0.f ? 1.f / l_run[r] : 0.f;
 #pragma unroll
-      for (int u = 0; u < DU; ++u)
-        __builtin_nontemporal_store(o[r][u], reinterpret_cast<f32x4*>(p.part_o + prow * D + 16 * u + 4 * q4));
+      for (int u = 0; u < DU; ++u) {
+        bf16x4 h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = static_cast<__bf16>(o[r][u][i] * inv);
+        __builtin_nontemporal_store(h, reinterpret_cast<bf16x4*>(p.part_o + prow * D + 16 * u + 4 * q4));
+      }
       if (q4 == 0) {
         __builtin_nontemporal_store(m_run[r], p.part_ml + prow * 2);
         __builtin_nontemporal_store(l_run[r], p.part_ml + prow * 2 + 1);
@@ -752,13 +759,14 @@ void attn_bf16_kernel(Params p) {
 }
 
 // Merge of split partials: m = max m_s, l = sum 2^(m_s - m) l_s,
-// o = sum 2^(m_s - m) o_s / l, lse = (m + log2 l) ln 2. One row per D/4
+// o = sum 2^(m_s - m) l_s o_s / l (o_s the split's own average, bf16),
+// lse = (m + log2 l) ln 2. One row per D/4
 // lanes; the partials of 16 splits are loaded at once (one round trip), and
 // longer split lists are folded in chunks with the same online rescaling.
 // Every (split, row) pair holds a partial or an empty marker (m = -inf),
 // whose o is never read into the sums.
 template <int D, typename OutT>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(256) void combine_kernel(const __bf16* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       int64_t R_tot, int32_t splits,
                                                       OutT* __restrict__ out, float* __restrict__ lse) {
@@ -772,13 +780,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < splits; s0 += CH) {
     float2 ml[CH];
-    f32x4 os[CH];
+    bf16x4 os[CH];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       const int64_t pr = (int64_t)(s0 + j) * R_tot + row;
       const bool ok = s0 + j < splits;
       ml[j] = ok ? *reinterpret_cast<const float2*>(part_ml + pr * 2) : float2{-INFINITY, 0.f};
-      os[j] = ok ? *reinterpret_cast<const f32x4*>(part_o + pr * D + 4 * sub) : f32x4{0.f, 0.f, 0.f, 0.f};
+      os[j] = ok ? *reinterpret_cast<const bf16x4*>(part_o + pr * D + 4 * sub) : bf16x4{};
     }
     float mc = m;
 #pragma unroll
@@ -791,8 +799,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     for (int j = 0; j < CH; ++j) {
       const bool live = ml[j].x != -INFINITY;
       const float w = live ? __builtin_amdgcn_exp2f(ml[j].x - mc) : 0.f;
-      l += w * ml[j].y;
-      acc = live ? acc + w * os[j] : acc;
+      const float wl = w * ml[j].y;
+      l += wl;
+      f32x4 o4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o4[i] = static_cast<float>(os[j][i]);
+      acc = live ? acc + wl * o4 : acc;
     }
     m = mc;
   }
@@ -960,7 +972,7 @@ AttnPlan plan_attn(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_
   pl.splits = (int)((tiles + tps - 1) / tps);
   if (pl.splits > 1) {
     const size_t rtot = (size_t)total_nodes * hq;
-    const size_t o_bytes = (size_t)pl.splits * rtot * head_dim * sizeof(float);
+    const size_t o_bytes = (size_t)pl.splits * rtot * head_dim * sizeof(__bf16);
     const size_t ml_bytes = (size_t)pl.splits * rtot * 2 * sizeof(float);
     pl.workspace = ((o_bytes + 255) & ~(size_t)255) + ((ml_bytes + 255) & ~(size_t)255);
   } else {
@@ -1010,8 +1022,8 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t stre
   p.lse = a.lse;
   const size_t rtot = (size_t)a.total_nodes * a.hq;
   char* ws = static_cast<char*>(a.workspace);
-  p.part_o = reinterpret_cast<float*>(ws);
-  const size_t o_bytes = ((size_t)plan.splits * rtot * a.head_dim * sizeof(float) + 255) & ~(size_t)255;
+  p.part_o = reinterpret_cast<__bf16*>(ws);
+  const size_t o_bytes = ((size_t)plan.splits * rtot * a.head_dim * sizeof(__bf16) + 255) & ~(size_t)255;
   p.part_ml = plan.splits > 1 ? reinterpret_cast<float*>(ws + o_bytes) : nullptr;
   p.num_pages = a.num_pages;
   p.max_pages = a.max_pages;
