@@ -29,12 +29,12 @@
 //
 // Kernels (every node of the batch in parallel; each node's rows are cut into
 // S shares, one 256-thread workgroup each):
-//   round 0:  share partials of both softmax normalisers; share 0 also lists
+//   pass 0:   share partials of both softmax normalisers; share 0 also lists
 //             the node's children (index order, tokens in the vocabulary)
 //             with their uniforms.
-//   round k:  (k = 1 .. max_children + 1) combine the shares' partials of the
-//             round before and fix (beta_{k-1}, gamma_{k-1}); then, for a node
-//             with m children, k <= m: share partials of F(beta_k) (round 1
+//   pass k:   (k = 1 .. max_children + 1) combine the shares' partials of the
+//             pass before and fix (beta_{k-1}, gamma_{k-1}); then, for a node
+//             with m children, k <= m: share partials of F(beta_k) (pass 1
 //             also the draft mass outside the children's tokens); k = m + 1:
 //             share sums of the bonus distribution.
 //   walk:     one 1024-thread workgroup per request: at each node one parallel
@@ -49,9 +49,9 @@
 namespace tv {
 namespace {
 
-constexpr int kRoundThreads = 256;
-constexpr int kRoundWaves = kRoundThreads / 64;
-constexpr int kRoundUnroll = 8;  // units per thread in flight (a share is one sweep at 16,384 tokens)
+constexpr int kPassThreads = 256;
+constexpr int kPassWaves = kPassThreads / 64;
+constexpr int kPassUnroll = 8;  // units per thread in flight (a share is one sweep at 16,384 tokens)
 constexpr int kWalkThreads = 1024;
 constexpr int kWalkWaves = kWalkThreads / 64;
 constexpr int kMaxShares = 32;
@@ -85,7 +85,7 @@ struct SArgs {
   NodeInfo* node;    // [N]
   ChildInfo* child;  // [N][C]
   Step* step;        // [N][C + 1]
-  float4* part;      // [2][N][S] share partials, by round parity
+  float4* part;      // [2][N][S] share partials, by pass parity
   float* bonus;      // [N][S] share sums of the bonus distribution
   int32_t* accept_len;
   int32_t* path;
@@ -116,30 +116,30 @@ __device__ __forceinline__ void share(int64_t units, int S, int s, int64_t& u0, 
   u1 = min(units, u0 + per);
 }
 
-// Visit the units [u0, u1) of two rows, kRoundUnroll units per thread in
+// Visit the units [u0, u1) of two rows, kPassUnroll units per thread in
 // flight at once (loads from a clamped index, so that a thread's loads are
 // issued together); fn(ya, yb, unit, valid).
 template <typename T, bool VEC, typename Fn>
 __device__ __forceinline__ void for_units(const T* ra, const T* rb, int64_t u0, int64_t u1, Fn&& fn) {
   constexpr int W = VocabUnit<T, VEC>::W;
-  for (int64_t base = u0; base < u1; base += kRoundUnroll * kRoundThreads) {
-    float ya[kRoundUnroll][W], yb[kRoundUnroll][W];
+  for (int64_t base = u0; base < u1; base += kPassUnroll * kPassThreads) {
+    float ya[kPassUnroll][W], yb[kPassUnroll][W];
 #pragma unroll
-    for (int u = 0; u < kRoundUnroll; ++u) {
-      const int64_t j = min(base + u * kRoundThreads + (int64_t)threadIdx.x, u1 - 1);
+    for (int u = 0; u < kPassUnroll; ++u) {
+      const int64_t j = min(base + u * kPassThreads + (int64_t)threadIdx.x, u1 - 1);
       VocabUnit<T, VEC>::load(ra + j * W, ya[u]);
       VocabUnit<T, VEC>::load(rb + j * W, yb[u]);
     }
 #pragma unroll
-    for (int u = 0; u < kRoundUnroll; ++u) {
-      const int64_t j = base + u * kRoundThreads + threadIdx.x;
+    for (int u = 0; u < kPassUnroll; ++u) {
+      const int64_t j = base + u * kPassThreads + threadIdx.x;
       fn(ya[u], yb[u], j, j < u1);
     }
   }
 }
 
-// Sum over a round workgroup of two values per thread.
-__device__ float2 round_sum2(float x, float y, float2* s_red) {
+// Sum over a pass workgroup of two values per thread.
+__device__ float2 pass_sum2(float x, float y, float2* s_red) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     x += __shfl_xor(x, off, 64);
@@ -150,7 +150,7 @@ __device__ float2 round_sum2(float x, float y, float2* s_red) {
   __syncthreads();
   float2 r = s_red[0];
 #pragma unroll
-  for (int w = 1; w < kRoundWaves; ++w) {
+  for (int w = 1; w < kPassWaves; ++w) {
     r.x += s_red[w].x;
     r.y += s_red[w].y;
   }
@@ -159,11 +159,11 @@ __device__ float2 round_sum2(float x, float y, float2* s_red) {
 }
 
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kRoundThreads) void sampled_round0_kernel(SArgs a, const T* __restrict__ tl,
+__global__ __launch_bounds__(kPassThreads) void sampled_prep_kernel(SArgs a, const T* __restrict__ tl,
                                                                        const T* __restrict__ dl) {
   constexpr int W = VocabUnit<T, VEC>::W;
-  __shared__ MaxSum s_ms[kRoundWaves];
-  __shared__ int s_cnt[kRoundWaves];
+  __shared__ MaxSum s_ms[kPassWaves];
+  __shared__ int s_cnt[kPassWaves];
   const int g = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int64_t units = a.vocab / W;  // VEC only when vocab % W == 0
@@ -182,8 +182,8 @@ __global__ __launch_bounds__(kRoundThreads) void sampled_round0_kernel(SArgs a, 
     fold(mp, ya, a.c);
     fold(mq, yb, a.c);
   });
-  mp = block_merge<kRoundWaves>(mp, s_ms);
-  mq = block_merge<kRoundWaves>(mq, s_ms);
+  mp = block_merge<kPassWaves>(mp, s_ms);
+  mq = block_merge<kPassWaves>(mq, s_ms);
   if (tid == 0) a.part[(size_t)g * a.S + s] = make_float4(mp.m, mp.s, mq.m, mq.s);
   if (s != 0) return;
 
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kRoundThreads) void sampled_round0_kernel(SArgs a, 
   int m = 0;
   if (local >= 0 && local < n) {  // (uniform; false only for malformed offsets)
     ChildInfo* ch = a.child + (size_t)g * a.C;
-    for (int base = local + 1; base < n; base += kRoundThreads) {
+    for (int base = local + 1; base < n; base += kPassThreads) {
       const int ci = base + tid;
       int x = -1;
       bool is = false;
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kRoundThreads) void sampled_round0_kernel(SArgs a, 
       __syncthreads();
       int off = m, tot = 0;
 #pragma unroll
-      for (int w = 0; w < kRoundWaves; ++w) {
+      for (int w = 0; w < kPassWaves; ++w) {
         const int cnt = s_cnt[w];
         off += (w < wave) ? cnt : 0;
         tot += cnt;
@@ -241,11 +241,11 @@ __global__ __launch_bounds__(kRoundThreads) void sampled_round0_kernel(SArgs a, 
 }
 
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kRoundThreads) void sampled_round_kernel(SArgs a, int k,
+__global__ __launch_bounds__(kPassThreads) void sampled_pass_kernel(SArgs a, int k,
                                                                       const T* __restrict__ tl,
                                                                       const T* __restrict__ dl) {
   constexpr int W = VocabUnit<T, VEC>::W;
-  __shared__ float2 s_red[kRoundWaves];
+  __shared__ float2 s_red[kPassWaves];
   __shared__ ChildInfo s_ch[TV_MAX_SAMPLED_CHILDREN];
   const int g = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
   const bool lead = (s == 0 && tid == 0);
@@ -274,9 +274,9 @@ __global__ __launch_bounds__(kRoundThreads) void sampled_round_kernel(SArgs a, i
     for (int i = 0; i < S; ++i) snc += prev[i].y;
     ni.snc = snc;
   }
-  // the children: round 1 fills in the probabilities of their tokens and the
-  // repeated tokens, later rounds read them
-  for (int j = tid; j < m; j += kRoundThreads) {
+  // the children: pass 1 fills in the probabilities of their tokens and the
+  // repeated tokens, later passes read them
+  for (int j = tid; j < m; j += kPassThreads) {
     ChildInfo c = ch[j];
     if (k == 1) {
       c.P = prob(load_one(ra + c.tok), a.c, ni.lp);
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kRoundThreads) void sampled_round_kernel(SArgs a, i
   }
   __syncthreads();
   if (s == 0 && k == 1)
-    for (int j = tid; j < m; j += kRoundThreads) ch[j] = s_ch[j];
+    for (int j = tid; j < m; j += kPassThreads) ch[j] = s_ch[j];
   if (lead && k <= 2) a.node[g] = ni;
 
   // (beta_{k-1}, gamma_{k-1})
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kRoundThreads) void sampled_round_kernel(SArgs a, i
   int64_t u0, u1;
   share(units, S, s, u0, u1);
   if (k <= m) {
-    // share partial of F(beta_k); round 1 also the draft mass outside the children
+    // share partial of F(beta_k); pass 1 also the draft mass outside the children
     const float beta = cur.beta + cur.gamma * inv_mass(ni.snc, s_ch, m, k - 1);
     float f = 0.f, snc = 0.f;
     for_units<T, VEC>(ra, rb, u0, u1, [&](float (&ya)[W], float (&yb)[W], int64_t j, bool valid) {
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(kRoundThreads) void sampled_round_kernel(SArgs a, i
         }
       }
     });
-    const float2 r = round_sum2(f, snc, s_red);
+    const float2 r = pass_sum2(f, snc, s_red);
     if (tid == 0)
       a.part[(size_t)(k & 1) * a.total_nodes * S + (size_t)g * S + s] = make_float4(r.x, r.y, 0.f, 0.f);
   } else {
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(kRoundThreads) void sampled_round_kernel(SArgs a, i
         sum += fmaxf(0.f, __builtin_fmaf(-cur.beta, Q, P)) * ig;
       }
     });
-    const float2 r = round_sum2(sum, 0.f, s_red);
+    const float2 r = pass_sum2(sum, 0.f, s_red);
     if (tid == 0) a.bonus[(size_t)g * S + s] = r.x;
   }
 }
@@ -580,9 +580,9 @@ hipError_t run_sampled(const SArgs& a, const void* tl, const void* dl, hipStream
   const T* d = static_cast<const T*>(dl);
   if (a.total_nodes > 0) {
     const dim3 grid(a.total_nodes, a.S);
-    hipLaunchKernelGGL((sampled_round0_kernel<T, VEC>), grid, dim3(kRoundThreads), 0, stream, a, t, d);
+    hipLaunchKernelGGL((sampled_prep_kernel<T, VEC>), grid, dim3(kPassThreads), 0, stream, a, t, d);
     for (int k = 1; k <= a.C + 1; ++k)
-      hipLaunchKernelGGL((sampled_round_kernel<T, VEC>), grid, dim3(kRoundThreads), 0, stream, a, k,
+      hipLaunchKernelGGL((sampled_pass_kernel<T, VEC>), grid, dim3(kPassThreads), 0, stream, a, k,
                          t, d);
   }
   const size_t slot = walk_slot_bytes(a.C, a.S);
