@@ -73,6 +73,15 @@ def test_graft_tree_full_vocabulary(seed):
     assert got[0].max() >= 1
 
 
+def test_benchmark_input_and_launch():
+    # the exact input and launch shape bench.py times: one Graft tree, seed 2,
+    # 151,936-token bf16 logits (10 shares per row)
+    si = W.sampled_inputs(np.random.default_rng(2), [list(W.GRAFT_TREE_PARENT)], W.QWEN3_VOCAB)
+    got, ref = _run(si)
+    _compare(got, ref, max_ties=0)
+    assert got[0][0] >= 1
+
+
 @pytest.mark.parametrize("temperature", [0.6, 1.0, 1.7])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_small_trees_many_requests(temperature, dtype):
