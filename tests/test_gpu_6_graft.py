@@ -156,6 +156,17 @@ def test_update_row_shares(n, v, k, dtype, offset):
     np.testing.assert_array_equal(a.cpu().numpy(), oracle.graft_update(adj, exact, toks))
 
 
+def test_update_many_nodes_one_workgroup_per_row():
+    # thousands of verified nodes: one workgroup per row, many repeated tokens
+    rng = np.random.default_rng(45)
+    v, n, k = 2000, 3000, 16
+    adj = _table(rng, v, k)
+    logits = rng.normal(0, 2, size=(n, v)).astype(np.float32)
+    toks = rng.integers(0, v, size=n).astype(np.int32)
+    got, exact = _update(adj, logits, toks, torch.bfloat16)
+    np.testing.assert_array_equal(got, oracle.graft_update(adj, exact, toks))
+
+
 def test_update_then_retrieve_on_device():
     rng = np.random.default_rng(12)
     v, k = 30000, 4

@@ -93,6 +93,20 @@ def test_small_trees_many_requests(temperature, dtype):
     assert _compare(got, ref, max_ties=2) >= 46
 
 
+def test_many_requests_and_the_per_level_walk():
+    # 256 requests (one share per row: the walk reads a node per level when
+    # the request's tables do not fit its LDS), bf16, 4096-token vocabulary
+    rng = np.random.default_rng(44)
+    trees = [W.random_tree(rng, int(rng.integers(1, 31)), max_children=8) for _ in range(256)]
+    si = W.sampled_inputs(rng, trees, 4096, dtype=torch.bfloat16, spread=2.5, noise=0.8)
+    got, ref = _run(si)
+    assert _compare(got, ref, max_ties=3) >= 250
+    # the same batch with a node cap too large for the walk's LDS tables
+    got2, _ = _run(si, max_nodes=8192)
+    for x, y in zip(got, got2):
+        np.testing.assert_array_equal(x, y)
+
+
 def test_matches_greedy_acceptance_as_temperature_vanishes():
     rng = np.random.default_rng(7)
     trees = [W.random_tree(rng, int(rng.integers(2, 30)), max_children=5) for _ in range(32)]
