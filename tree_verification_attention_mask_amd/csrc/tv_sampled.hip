@@ -32,17 +32,20 @@
 //   pass 0:   share partials of both softmax normalisers; share 0 also lists
 //             the node's children (index order, tokens in the vocabulary)
 //             with their uniforms.
-//   pass k:   (k = 1 .. max_children + 1) combine the shares' partials of the
-//             pass before and fix (beta_{k-1}, gamma_{k-1}); then, for a node
-//             with m children, k <= m: share partials of F(beta_k) (pass 1
-//             also the draft mass outside the children's tokens); k = m + 1:
-//             share sums of the bonus distribution.
+//   pass k:   (k = 1 .. max_children) combine the shares' partials of the pass
+//             before and fix (beta_{k-1}, gamma_{k-1}) with each share's sum of
+//             that state's residual (the partial of F over F); then, for a
+//             node with m >= k children, share partials of F(beta_k) (pass 1
+//             also the draft mass outside the children's tokens).
 //   walk:     one 1024-thread workgroup per request: at each node one parallel
 //             read of its children and steps, the tests in order with scalar
-//             arithmetic every thread repeats, and for the bonus a scan of the
-//             share sums and an inverse transform inside the one share that
-//             holds the draw (per-thread runs in token order, a block scan,
-//             then a rescan of the one run).
+//             arithmetic every thread repeats; at the last node it fixes the
+//             final step from the last pass's partials, finds the share that
+//             holds the bonus draw from the share sums and inverts the CDF
+//             inside it (per-thread runs in token order, a block scan, then a
+//             rescan of the one run). The bonus distribution after the last
+//             step needs no sweep of its own: its share sums are the last
+//             F partials over F.
 #include "tv_launch.h"
 #include "tv_vocab.h"
 
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(kPassThreads) void sampled_pass_kernel(SArgs a, int
   const bool lead = (s == 0 && tid == 0);
   NodeInfo ni = a.node[g];
   const int m = ni.m;
-  if (k > m + 1) return;  // this node's chain and bonus are done (uniform)
+  if (k > (m > 1 ? m : 1)) return;  // pass 1 for every node, then while steps remain (uniform)
   const int S = a.S;
   const float4* prev = a.part + (size_t)((k - 1) & 1) * a.total_nodes * S + (size_t)g * S;
   ChildInfo* ch = a.child + (size_t)g * a.C;
@@ -297,14 +300,25 @@ __global__ __launch_bounds__(kPassThreads) void sampled_pass_kernel(SArgs a, int
 
   // (beta_{k-1}, gamma_{k-1})
   Step cur{0.f, 1.f};
+  float F = 0.f;
   if (k >= 2) {
     const Step pk = st[k - 2];
     const float beta = pk.beta + pk.gamma * inv_mass(ni.snc, s_ch, m, k - 2);
-    float F = 0.f;
     for (int i = 0; i < S; ++i) F += prev[i].x;
     cur = (F > 0.f) ? Step{beta, F} : pk;
   }
   if (lead) st[k - 1] = cur;
+  // this share's sum of the state's residual max(0, P - beta Q) / gamma, kept
+  // for the walk's bonus draw when a node's last step leaves p unchanged
+  if (tid == 0) {
+    float* bs = a.bonus + (size_t)g * S + s;
+    if (k == 1) {
+      const float4 p0 = prev[s];  // this share's (max, sum) of the target's exponents
+      *bs = (p0.x == -INFINITY) ? 0.f : p0.y * __builtin_amdgcn_exp2f(p0.x - ni.lp);
+    } else if (F > 0.f) {
+      *bs = prev[s].x / F;
+    }
+  }
 
   const int64_t units = a.vocab / W;
   int64_t u0, u1;
@@ -344,21 +358,6 @@ __global__ __launch_bounds__(kPassThreads) void sampled_pass_kernel(SArgs a, int
     const float2 r = pass_sum2(f, snc, s_red);
     if (tid == 0)
       a.part[(size_t)(k & 1) * a.total_nodes * S + (size_t)g * S + s] = make_float4(r.x, r.y, 0.f, 0.f);
-  } else {
-    // k = m + 1: share sum of the bonus distribution max(0, P - beta Q) / gamma
-    const float ig = 1.f / cur.gamma;
-    float sum = 0.f;
-    for_units<T, VEC>(ra, rb, u0, u1, [&](float (&ya)[W], float (&yb)[W], int64_t, bool valid) {
-      if (!valid) return;
-#pragma unroll
-      for (int e = 0; e < W; ++e) {
-        const float P = prob(ya[e], a.c, ni.lp);
-        const float Q = prob(yb[e], a.c, ni.lq);
-        sum += fmaxf(0.f, __builtin_fmaf(-cur.beta, Q, P)) * ig;
-      }
-    });
-    const float2 r = pass_sum2(sum, 0.f, s_red);
-    if (tid == 0) a.bonus[(size_t)g * S + s] = r.x;
   }
 }
 
@@ -387,12 +386,13 @@ __device__ float walk_inclusive_sum(float v, float* s_w, float& total) {
 }
 
 // Walk storage in dynamic LDS: K node slots of children [K][C], steps
-// [K][C + 1], node info [K] and share sums [K][S]. K = the request's node cap
+// [K][C + 1], node info [K], share sums [K][S] and the share partials of F of
+// both pass parities [K][2][S]. K = the request's node cap
 // when that fits (everything is read once, up front), else 1 (one node read
 // per level).
 __host__ __device__ inline size_t walk_slot_bytes(int C, int S) {
   return (size_t)C * sizeof(ChildInfo) + (size_t)(C + 1) * sizeof(Step) + sizeof(NodeInfo) +
-         (size_t)S * sizeof(float);
+         (size_t)3 * S * sizeof(float);
 }
 constexpr size_t kWalkPreloadBytes = 48 * 1024;
 
@@ -425,6 +425,7 @@ __global__ __launch_bounds__(kWalkThreads) void sampled_walk_kernel(SArgs a, int
   Step* s_sts = reinterpret_cast<Step*>(s_chs + (size_t)K * C);
   NodeInfo* s_nis = reinterpret_cast<NodeInfo*>(s_sts + (size_t)K * (C + 1));
   float* s_shs = reinterpret_cast<float*>(s_nis + K);
+  float* s_pms = s_shs + (size_t)K * S;
   // copy nodes [first, first + cnt) of the request into slots [0, cnt)
   auto fetch = [&](int first, int cnt) {
     const size_t g0 = (size_t)lo + first;
@@ -432,6 +433,11 @@ __global__ __launch_bounds__(kWalkThreads) void sampled_walk_kernel(SArgs a, int
     for (int i = tid; i < cnt * (C + 1); i += kWalkThreads) s_sts[i] = a.step[g0 * (C + 1) + i];
     for (int i = tid; i < cnt; i += kWalkThreads) s_nis[i] = a.node[g0 + i];
     for (int i = tid; i < cnt * S; i += kWalkThreads) s_shs[i] = a.bonus[g0 * S + i];
+    for (int i = tid; i < 2 * cnt * S; i += kWalkThreads) {
+      const int par = i / (cnt * S), r = i % (cnt * S);  // [parity][node][share] -> slot [node][parity][share]
+      s_pms[(r / S) * 2 * S + par * S + r % S] =
+          a.part[(size_t)par * a.total_nodes * S + g0 * S + r].x;
+    }
   };
   if (preload) fetch(0, n);
   __syncthreads();
@@ -450,6 +456,7 @@ __global__ __launch_bounds__(kWalkThreads) void sampled_walk_kernel(SArgs a, int
     const float* s_share = s_shs + (size_t)slot * S;
     const NodeInfo ni = s_nis[slot];
     const int m = ni.m;
+    const float* s_pm = s_pms + ((size_t)slot * 2 + (m & 1)) * S;  // the last pass's partials
     // the children in order (every thread takes the same decisions)
     int next = -1;
     for (int l = 0; l < m; ++l) {
@@ -475,17 +482,30 @@ __global__ __launch_bounds__(kWalkThreads) void sampled_walk_kernel(SArgs a, int
       continue;
     }
 
-    // bonus: the share that holds the draw, then inverse transform inside it
-    const Step fin = s_st[m];
+    // bonus. The node's last step is fixed here from the last pass's share
+    // partials of F (as a pass would fix it); the state's per-share sums are
+    // those partials over F, or, when the step left p unchanged, the sums the
+    // passes kept.
+    Step fin{0.f, 1.f};
+    float Fm = 0.f;
+    if (m >= 1) {
+      const Step pk = s_st[m - 1];
+      const float beta = pk.beta + pk.gamma * inv_mass(ni.snc, s_ch, m, m - 1);
+      for (int i = 0; i < S; ++i) Fm += s_pm[i];
+      fin = (Fm > 0.f) ? Step{beta, Fm} : pk;
+    }
+    const bool fresh = Fm > 0.f;
+    auto share_sum = [&](int i) { return fresh ? s_pm[i] / Fm : s_share[i]; };
     const float ig = 1.f / fin.gamma;
     float total = 0.f;
-    for (int i = 0; i < S; ++i) total += s_share[i];
+    for (int i = 0; i < S; ++i) total += share_sum(i);
     const float target = a.u_bonus[b] * total;
     int sh = -1, last_sh = -1;
     float before = 0.f, acc = 0.f;
     for (int i = 0; i < S; ++i) {
-      const float nx = acc + s_share[i];
-      if (s_share[i] > 0.f) last_sh = i;
+      const float si = share_sum(i);
+      const float nx = acc + si;
+      if (si > 0.f) last_sh = i;
       if (sh < 0 && acc <= target && target < nx) {
         sh = i;
         before = acc;
@@ -581,7 +601,7 @@ hipError_t run_sampled(const SArgs& a, const void* tl, const void* dl, hipStream
   if (a.total_nodes > 0) {
     const dim3 grid(a.total_nodes, a.S);
     hipLaunchKernelGGL((sampled_prep_kernel<T, VEC>), grid, dim3(kPassThreads), 0, stream, a, t, d);
-    for (int k = 1; k <= a.C + 1; ++k)
+    for (int k = 1; k <= a.C; ++k)
       hipLaunchKernelGGL((sampled_pass_kernel<T, VEC>), grid, dim3(kPassThreads), 0, stream, a, k,
                          t, d);
   }
