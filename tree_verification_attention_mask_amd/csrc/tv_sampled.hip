@@ -57,6 +57,8 @@ constexpr int kPassWaves = kPassThreads / 64;
 constexpr int kPassUnroll = 8;  // units per thread in flight (a share is one sweep at 16,384 tokens)
 constexpr int kWalkThreads = 1024;
 constexpr int kWalkWaves = kWalkThreads / 64;
+constexpr int kFetchUnroll = 8;  // words a walk thread has in flight while copying tables
+constexpr int kWalkCache = 2;    // bonus units a walk thread keeps in registers
 constexpr int kMaxShares = 32;
 constexpr float kLog2eS = 1.4426950408889634f;
 
@@ -64,6 +66,7 @@ struct NodeInfo {
   float lp, lq;  // log2 normalisers: P(v) = 2^(c a_v - lp), Q(v) = 2^(c b_v - lq)
   float snc;     // draft mass outside the children's tokens
   int32_t m;     // children kept (tokens in the vocabulary), at most max_children
+  int32_t next;  // the first child that passes its test (request-local index), or -1
 };
 struct ChildInfo {
   int32_t tok, local;  // token, request-local node index
@@ -239,6 +242,7 @@ __global__ __launch_bounds__(kPassThreads) void sampled_prep_kernel(SArgs a, con
   if (tid == 0) {
     NodeInfo ni{};
     ni.m = min(m, a.C);
+    ni.next = -1;
     a.node[g] = ni;
   }
 }
@@ -250,11 +254,17 @@ __global__ __launch_bounds__(kPassThreads) void sampled_pass_kernel(SArgs a, int
   constexpr int W = VocabUnit<T, VEC>::W;
   __shared__ float2 s_red[kPassWaves];
   __shared__ ChildInfo s_ch[TV_MAX_SAMPLED_CHILDREN];
+  __shared__ Step s_st[TV_MAX_SAMPLED_CHILDREN];
   const int g = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const bool lead = (s == 0 && tid == 0);
   NodeInfo ni = a.node[g];
   const int m = ni.m;
-  if (k > (m > 1 ? m : 1)) return;  // pass 1 for every node, then while steps remain (uniform)
+  const int last = m > 1 ? m : 1;
+  if (k > last) return;  // pass 1 for every node, then while steps remain (uniform)
+  // the node's last pass fixes (beta_{m-1}, gamma_{m-1}): after it every
+  // child's test is known, and share 0 takes them
+  const bool tests = (s == 0 && k == last);
   const int S = a.S;
   const float4* prev = a.part + (size_t)((k - 1) & 1) * a.total_nodes * S + (size_t)g * S;
   ChildInfo* ch = a.child + (size_t)g * a.C;
@@ -293,6 +303,8 @@ __global__ __launch_bounds__(kPassThreads) void sampled_pass_kernel(SArgs a, int
     }
     s_ch[j] = c;
   }
+  if (tests)
+    for (int l = tid; l < k - 1; l += kPassThreads) s_st[l] = st[l];
   __syncthreads();
   if (s == 0 && k == 1)
     for (int j = tid; j < m; j += kPassThreads) ch[j] = s_ch[j];
@@ -308,6 +320,38 @@ __global__ __launch_bounds__(kPassThreads) void sampled_pass_kernel(SArgs a, int
     cur = (F > 0.f) ? Step{beta, F} : pk;
   }
   if (lead) st[k - 1] = cur;
+  if (tests) {
+    // the children's tests, one lane each (a test depends on no earlier
+    // outcome, only on the state its child meets); the first that passes
+    if (tid == 0) s_st[k - 1] = cur;
+    __syncthreads();
+    if (wave == 0) {
+      int first = -1;
+      for (int l0 = 0; l0 < m; l0 += 64) {
+        const int l = l0 + lane;
+        bool acc = false;
+        if (l < m) {
+          const ChildInfo c = s_ch[l];
+          const Step sl = s_st[l];
+          float p, q;
+          if (c.dup >= 0) {  // its token was rejected before: q is 0, the residual frozen
+            q = 0.f;
+            p = fmaxf(0.f, __builtin_fmaf(-s_st[c.dup + 1].beta, c.Q, c.P)) / sl.gamma;
+          } else {
+            q = c.Q * inv_mass(ni.snc, s_ch, m, l);
+            p = fmaxf(0.f, __builtin_fmaf(-sl.beta, c.Q, c.P)) / sl.gamma;
+          }
+          acc = c.u * q < p;
+        }
+        const uint64_t bal = __ballot(acc);
+        if (bal != 0) {
+          first = s_ch[l0 + __ffsll((unsigned long long)bal) - 1].local;
+          break;
+        }
+      }
+      if (lane == 0) a.node[g].next = first;
+    }
+  }
   // this share's sum of the state's residual max(0, P - beta Q) / gamma, kept
   // for the walk's bonus draw when a node's last step leaves p unchanged
   if (tid == 0) {
@@ -361,16 +405,36 @@ __global__ __launch_bounds__(kPassThreads) void sampled_pass_kernel(SArgs a, int
   }
 }
 
+// The value of the lane that DPP control CTRL names, 0 where there is none
+// (a shift past the row's or the wave's edge, or a row ROWS leaves out).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_in(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, false));
+}
+
+// Inclusive prefix sum over a wave in lane order: shifts by 1, 2, 4, 8 inside
+// each row of 16 lanes, then the last lane of a row added into the next rows
+// (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3).
+__device__ __forceinline__ float wave_incl_sum(float x) {
+  x += dpp_in<0x111, 0xf>(x);
+  x += dpp_in<0x112, 0xf>(x);
+  x += dpp_in<0x114, 0xf>(x);
+  x += dpp_in<0x118, 0xf>(x);
+  x += dpp_in<0x142, 0xa>(x);
+  x += dpp_in<0x143, 0xc>(x);
+  return x;
+}
+
+// The previous lane's value (wave_shr:1), 0 in lane 0.
+__device__ __forceinline__ float wave_prev(float x) { return dpp_in<0x138, 0xf>(x); }
+
 // Inclusive prefix sum over the walk block of one value per thread, in thread
-// order; returns the thread's inclusive sum and the block total.
-__device__ float walk_inclusive_sum(float v, float* s_w, float& total) {
+// order; returns the thread's inclusive sum, the block total and, in `excl`,
+// the previous thread's inclusive sum (0 for thread 0), formed by the same
+// additions, so that the runs [excl, incl) tile [0, total) exactly.
+__device__ float walk_inclusive_sum(float v, float* s_w, float& total, float& excl) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float o = __shfl_up(x, off, 64);
-    if (lane >= off) x += o;
-  }
+  const float x = wave_incl_sum(v);
   if (lane == 63) s_w[wave] = x;
   __syncthreads();
   float before = 0.f;
@@ -381,7 +445,10 @@ __device__ float walk_inclusive_sum(float v, float* s_w, float& total) {
     before += (w < wave) ? t : 0.f;
     total += t;
   }
-  __syncthreads();
+  // lane 0's predecessor is lane 63 of the wave before, whose inclusive sum
+  // is that wave's `before` plus its lane-63 value: exactly this `before`
+  const float xp = wave_prev(x);
+  excl = (lane == 0) ? before : before + xp;
   return before + x;
 }
 
@@ -396,14 +463,24 @@ __host__ __device__ inline size_t walk_slot_bytes(int C, int S) {
 }
 constexpr size_t kWalkPreloadBytes = 48 * 1024;
 
+// What the walk's first wave hands the block for the bonus draw.
+struct BonusPick {
+  int32_t node, slot, depth;  // the last node (request-local), its slot, the accepted length
+  int32_t sh;                 // the share that holds the draw (-1: none)
+  float beta, ig;           // the final state: residual max(0, P - beta Q) * ig
+  float t;                  // the draw's offset inside share `sh` (+inf: the last token with mass)
+};
+
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kWalkThreads) void sampled_walk_kernel(SArgs a, int preload,
                                                                     const T* __restrict__ tl,
                                                                     const T* __restrict__ dl) {
   constexpr int W = VocabUnit<T, VEC>::W;
   extern __shared__ float4 s_dyn4[];
-  __shared__ float s_w[kWalkWaves], s_incl[kWalkWaves];
-  __shared__ int s_pick, s_last;
+  __shared__ float s_w[kWalkWaves];
+  __shared__ int s_lastw[kWalkWaves];
+  __shared__ int s_pick, s_fb;
+  __shared__ BonusPick s_bp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
   const int lo = clampi(a.cu_nodes[b], 0, a.total_nodes);
@@ -419,6 +496,7 @@ __global__ __launch_bounds__(kWalkThreads) void sampled_walk_kernel(SArgs a, int
     }
     return;
   }
+  const float ub = a.u_bonus[b];  // read now: its latency hides under the table copy
   const int C = a.C, S = a.S;
   const int K = preload ? a.max_nodes : 1;
   ChildInfo* s_chs = reinterpret_cast<ChildInfo*>(s_dyn4);
@@ -426,171 +504,237 @@ __global__ __launch_bounds__(kWalkThreads) void sampled_walk_kernel(SArgs a, int
   NodeInfo* s_nis = reinterpret_cast<NodeInfo*>(s_sts + (size_t)K * (C + 1));
   float* s_shs = reinterpret_cast<float*>(s_nis + K);
   float* s_pms = s_shs + (size_t)K * S;
-  // copy nodes [first, first + cnt) of the request into slots [0, cnt)
+  // copy nodes [first, first + cnt) of the request into slots [0, cnt): the
+  // five tables are one run of 32-bit words (the F partials' .x of both
+  // parities last), copied kFetchUnroll words a thread at a time with every
+  // load issued before the first LDS store, so the copy is one round trip
   auto fetch = [&](int first, int cnt) {
     const size_t g0 = (size_t)lo + first;
-    for (int i = tid; i < cnt * C; i += kWalkThreads) s_chs[i] = a.child[g0 * C + i];
-    for (int i = tid; i < cnt * (C + 1); i += kWalkThreads) s_sts[i] = a.step[g0 * (C + 1) + i];
-    for (int i = tid; i < cnt; i += kWalkThreads) s_nis[i] = a.node[g0 + i];
-    for (int i = tid; i < cnt * S; i += kWalkThreads) s_shs[i] = a.bonus[g0 * S + i];
-    for (int i = tid; i < 2 * cnt * S; i += kWalkThreads) {
-      const int par = i / (cnt * S), r = i % (cnt * S);  // [parity][node][share] -> slot [node][parity][share]
-      s_pms[(r / S) * 2 * S + par * S + r % S] =
-          a.part[(size_t)par * a.total_nodes * S + g0 * S + r].x;
+    const uint32_t* src_ch = reinterpret_cast<const uint32_t*>(a.child + g0 * C);
+    const uint32_t* src_st = reinterpret_cast<const uint32_t*>(a.step + g0 * (C + 1));
+    const uint32_t* src_ni = reinterpret_cast<const uint32_t*>(a.node + g0);
+    const uint32_t* src_sh = reinterpret_cast<const uint32_t*>(a.bonus + g0 * S);
+    const uint32_t* src_pm = reinterpret_cast<const uint32_t*>(a.part + g0 * S);
+    const size_t par_words = (size_t)a.total_nodes * S * 4;  // float4 words of one parity
+    const int cs = cnt * S;
+    const int e_ch = cnt * C * (int)(sizeof(ChildInfo) / 4);
+    const int e_st = e_ch + cnt * (C + 1) * (int)(sizeof(Step) / 4);
+    const int e_ni = e_st + cnt * (int)(sizeof(NodeInfo) / 4);
+    const int e_sh = e_ni + cs;
+    const int total = e_sh + 2 * cs;
+    uint32_t* dst_ch = reinterpret_cast<uint32_t*>(s_chs);
+    uint32_t* dst_st = reinterpret_cast<uint32_t*>(s_sts);
+    uint32_t* dst_ni = reinterpret_cast<uint32_t*>(s_nis);
+    uint32_t* dst_sh = reinterpret_cast<uint32_t*>(s_shs);
+    uint32_t* dst_pm = reinterpret_cast<uint32_t*>(s_pms);
+    for (int base = tid; base < total; base += kWalkThreads * kFetchUnroll) {
+      uint32_t v[kFetchUnroll];
+#pragma unroll
+      for (int u = 0; u < kFetchUnroll; ++u) {
+        const int i = min(base + u * kWalkThreads, total - 1);  // clamped: every load in bounds
+        const uint32_t* src;
+        if (i < e_ch) src = src_ch + i;
+        else if (i < e_st) src = src_st + (i - e_ch);
+        else if (i < e_ni) src = src_ni + (i - e_st);
+        else if (i < e_sh) src = src_sh + (i - e_ni);
+        else {
+          const int r = i - e_sh, par = r >= cs ? 1 : 0;
+          src = src_pm + par * par_words + (size_t)(r - par * cs) * 4;
+        }
+        v[u] = *src;
+      }
+#pragma unroll
+      for (int u = 0; u < kFetchUnroll; ++u) {
+        const int i = base + u * kWalkThreads;
+        if (i >= total) break;
+        uint32_t* dst;
+        if (i < e_ch) dst = dst_ch + i;
+        else if (i < e_st) dst = dst_st + (i - e_ch);
+        else if (i < e_ni) dst = dst_ni + (i - e_st);
+        else if (i < e_sh) dst = dst_sh + (i - e_ni);
+        else {  // [parity][node][share] -> slot [node][parity][share]
+          const int r = i - e_sh, par = r >= cs ? 1 : 0, q = r - par * cs;
+          dst = dst_pm + (q / S) * 2 * S + par * S + q % S;
+        }
+        *dst = v[u];
+      }
     }
   };
-  if (preload) fetch(0, n);
-  __syncthreads();
-  const int64_t units = a.vocab / W;
 
-  int node = 0, depth = 0;
-  for (;;) {
-    const int g = lo + node;
-    if (!preload) {  // one round trip for the node, all its slots
-      fetch(node, 1);
-      __syncthreads();
-    }
-    const int slot = preload ? node : 0;
+  // First wave only. The bonus draw at the node in `slot`: the node's last
+  // step is fixed from the last pass's share partials of F (as a pass would
+  // fix it); the state's share sums are those partials over F or, when the
+  // step left p unchanged, the sums the passes kept; a wave scan of the share
+  // sums (S <= 64) finds the share that holds u * total.
+  auto pick_share = [&](int node, int slot, int depth) {
     const ChildInfo* s_ch = s_chs + (size_t)slot * C;
     const Step* s_st = s_sts + (size_t)slot * (C + 1);
     const float* s_share = s_shs + (size_t)slot * S;
     const NodeInfo ni = s_nis[slot];
     const int m = ni.m;
     const float* s_pm = s_pms + ((size_t)slot * 2 + (m & 1)) * S;  // the last pass's partials
-    // the children in order (every thread takes the same decisions)
-    int next = -1;
-    for (int l = 0; l < m; ++l) {
-      const ChildInfo c = s_ch[l];
-      float p, q;
-      if (c.dup >= 0) {  // its token was rejected before: q is 0, the residual frozen
-        q = 0.f;
-        p = fmaxf(0.f, __builtin_fmaf(-s_st[c.dup + 1].beta, c.Q, c.P)) / s_st[l].gamma;
-      } else {
-        q = c.Q * inv_mass(ni.snc, s_ch, m, l);
-        p = fmaxf(0.f, __builtin_fmaf(-s_st[l].beta, c.Q, c.P)) / s_st[l].gamma;
-      }
-      if (c.u * q < p) {
-        next = c.local;
-        break;
-      }
-    }
-    if (next > node && next < n) {
-      node = next;
-      ++depth;
-      if (tid == 0 && depth <= a.max_depth) path[depth] = node;
-      if (!preload) __syncthreads();  // slot 0 is refilled for the next node
-      continue;
-    }
-
-    // bonus. The node's last step is fixed here from the last pass's share
-    // partials of F (as a pass would fix it); the state's per-share sums are
-    // those partials over F, or, when the step left p unchanged, the sums the
-    // passes kept.
+    const float pm = lane < S ? s_pm[lane] : 0.f;
     Step fin{0.f, 1.f};
     float Fm = 0.f;
     if (m >= 1) {
       const Step pk = s_st[m - 1];
       const float beta = pk.beta + pk.gamma * inv_mass(ni.snc, s_ch, m, m - 1);
-      for (int i = 0; i < S; ++i) Fm += s_pm[i];
+      Fm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_incl_sum(pm)), 63));
       fin = (Fm > 0.f) ? Step{beta, Fm} : pk;
     }
-    const bool fresh = Fm > 0.f;
-    auto share_sum = [&](int i) { return fresh ? s_pm[i] / Fm : s_share[i]; };
-    const float ig = 1.f / fin.gamma;
-    float total = 0.f;
-    for (int i = 0; i < S; ++i) total += share_sum(i);
-    const float target = a.u_bonus[b] * total;
-    int sh = -1, last_sh = -1;
-    float before = 0.f, acc = 0.f;
-    for (int i = 0; i < S; ++i) {
-      const float si = share_sum(i);
-      const float nx = acc + si;
-      if (si > 0.f) last_sh = i;
-      if (sh < 0 && acc <= target && target < nx) {
-        sh = i;
-        before = acc;
-      }
-      acc = nx;
+    const float si = lane < S ? ((Fm > 0.f) ? pm / Fm : s_share[lane]) : 0.f;
+    const float incl = wave_incl_sum(si);
+    const float excl = wave_prev(incl);
+    const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
+    const float target = ub * total;
+    const uint64_t in = __ballot(excl <= target && target < incl);
+    const uint64_t mass = __ballot(si > 0.f);
+    int sh = -1;
+    float t = INFINITY;
+    if (in != 0) {
+      sh = __ffsll((unsigned long long)in) - 1;
+      t = target - __int_as_float(__builtin_amdgcn_readlane(__float_as_int(excl), sh));
+    } else if (mass != 0) {  // at or past the total: the last token with mass
+      sh = 63 - __clzll((unsigned long long)mass);
     }
-    const bool past = sh < 0;  // at or past the total: the last token with mass
-    if (past) sh = last_sh;
-    int pick = -1;
-    if (sh >= 0) {
-      int64_t u0, u1;
-      share(units, S, sh, u0, u1);
-      const int64_t per = (u1 - u0 + kWalkThreads - 1) / kWalkThreads;
-      const int64_t j0 = min(u1, u0 + (int64_t)tid * per), j1 = min(u1, j0 + per);
-      const T* ra = tl + (int64_t)g * a.vocab;
-      const T* rb = dl + (int64_t)g * a.vocab;
-      auto p_at = [&](int64_t j, float (&pv)[W]) {
-        float ya[W], yb[W];
-        VocabUnit<T, VEC>::load(ra + j * W, ya);
-        VocabUnit<T, VEC>::load(rb + j * W, yb);
+    if (lane == 0) s_bp = BonusPick{node, slot, depth, sh, fin.beta, 1.f / fin.gamma, t};
+  };
+
+  if (preload) fetch(0, n);
+  __syncthreads();
+  int node = 0, depth = 0;
+  if (preload) {
+    // the whole walk in the first wave, from the copied tables
+    if (wave == 0) {
+      for (;;) {
+        const int next = s_nis[node].next;
+        if (!(next > node && next < n)) break;
+        node = next;
+        ++depth;
+        if (lane == 0 && depth <= a.max_depth) path[depth] = node;
+      }
+      pick_share(node, node, depth);
+    }
+  } else {
+    for (;;) {  // one node's tables a level, read by the block
+      fetch(node, 1);
+      __syncthreads();
+      const int next = s_nis[0].next;
+      __syncthreads();  // every thread has read slot 0 before it is refilled
+      if (!(next > node && next < n)) break;
+      node = next;
+      ++depth;
+      if (tid == 0 && depth <= a.max_depth) path[depth] = node;
+    }
+    if (wave == 0) pick_share(node, 0, depth);
+  }
+  if (tid == 0) {
+    s_pick = -1;
+    s_fb = -1;
+  }
+  __syncthreads();
+  const BonusPick bp = s_bp;
+  const int g = lo + bp.node;
+  int pick = -1;
+  if (bp.sh >= 0) {
+    const NodeInfo ni = s_nis[bp.slot];
+    const int64_t units = a.vocab / W;
+    int64_t u0, u1;
+    share(units, S, bp.sh, u0, u1);
+    const int64_t per = (u1 - u0 + kWalkThreads - 1) / kWalkThreads;
+    const int64_t j0 = min(u1, u0 + (int64_t)tid * per), j1 = min(u1, j0 + per);
+    const T* ra = tl + (int64_t)g * a.vocab;
+    const T* rb = dl + (int64_t)g * a.vocab;
+    auto p_at = [&](int64_t j, float (&pv)[W]) {
+      float ya[W], yb[W];
+      VocabUnit<T, VEC>::load(ra + j * W, ya);
+      VocabUnit<T, VEC>::load(rb + j * W, yb);
+#pragma unroll
+      for (int e = 0; e < W; ++e) {
+        const float P = prob(ya[e], a.c, ni.lp);
+        const float Q = prob(yb[e], a.c, ni.lq);
+        pv[e] = fmaxf(0.f, __builtin_fmaf(-bp.beta, Q, P)) * bp.ig;
+      }
+    };
+    // per-thread runs in token order; the thread's first kWalkCache units
+    // stay in registers for the rescan (a clamped load of unit 0 stands in
+    // past the run's end, then zeroed)
+    float pc[kWalkCache][W];
+    float run = 0.f;
+#pragma unroll
+    for (int c = 0; c < kWalkCache; ++c) {
+      const bool ok = j0 + c < j1;
+      p_at(ok ? j0 + c : 0, pc[c]);
+#pragma unroll
+      for (int e = 0; e < W; ++e) {
+        pc[c][e] = ok ? pc[c][e] : 0.f;
+        run += pc[c][e];
+      }
+    }
+    for (int64_t j = j0 + kWalkCache; j < j1; ++j) {
+      float pv[W];
+      p_at(j, pv);
+#pragma unroll
+      for (int e = 0; e < W; ++e) run += pv[e];
+    }
+    const uint64_t has = __ballot(run > 0.f);
+    if (lane == 0) s_lastw[wave] = has ? wave * 64 + 63 - __clzll((unsigned long long)has) : -1;
+    float stotal, excl;
+    const float incl = walk_inclusive_sum(run, s_w, stotal, excl);
+    if (excl <= bp.t && bp.t < incl) {
+      // the same additions in the same order as the run's sum
+      float r = excl;
+      int pk = -1, last = -1;
+      auto visit = [&](int64_t j, const float (&pv)[W]) {
 #pragma unroll
         for (int e = 0; e < W; ++e) {
-          const float P = prob(ya[e], a.c, ni.lp);
-          const float Q = prob(yb[e], a.c, ni.lq);
-          pv[e] = fmaxf(0.f, __builtin_fmaf(-fin.beta, Q, P)) * ig;
+          if (pk >= 0) break;
+          if (pv[e] > 0.f) last = (int)(j * W + e);
+          r += pv[e];
+          if (r > bp.t && pv[e] > 0.f) pk = (int)(j * W + e);
         }
       };
-      float run = 0.f;
-      for (int64_t j = j0; j < j1; ++j) {
+#pragma unroll
+      for (int c = 0; c < kWalkCache; ++c)
+        if (j0 + c < j1 && pk < 0) visit(j0 + c, pc[c]);
+      for (int64_t j = j0 + kWalkCache; j < j1 && pk < 0; ++j) {
         float pv[W];
         p_at(j, pv);
+        visit(j, pv);
+      }
+      s_pick = pk >= 0 ? pk : last;
+    }
+    __syncthreads();
+    pick = s_pick;  // not written again: the fallback has its own slot
+    if (pick < 0) {  // (uniform)
+      // the draw fell outside every run (+inf, or rounding): the last token
+      // with mass, in the last run that has some
+      int lt = -1;
 #pragma unroll
-        for (int e = 0; e < W; ++e) run += pv[e];
-      }
-      float stotal;
-      const float incl = walk_inclusive_sum(run, s_w, stotal);
-      // the previous thread's inclusive sum: a shuffle within the wave, LDS
-      // across waves, so the runs [excl, incl) tile [0, stotal) exactly
-      if (lane == 63) s_incl[wave] = incl;
-      if (tid == 0) {
-        s_pick = -1;
-        s_last = -1;
-      }
-      __syncthreads();
-      float excl = __shfl_up(incl, 1, 64);
-      if (lane == 0) excl = (wave == 0) ? 0.f : s_incl[wave - 1];
-      const float t = past ? INFINITY : target - before;
-      if (excl <= t && t < incl) {
-        float r = excl;
-        int pk = -1, last = -1;
-        for (int64_t j = j0; j < j1 && pk < 0; ++j) {
-          float pv[W];
-          p_at(j, pv);
-#pragma unroll
-          for (int e = 0; e < W; ++e) {
-            if (pk >= 0) break;
-            if (pv[e] > 0.f) last = (int)(j * W + e);
-            r += pv[e];
-            if (r > t && pv[e] > 0.f) pk = (int)(j * W + e);
-          }
-        }
-        s_pick = pk >= 0 ? pk : last;
-      }
-      if (run > 0.f) atomicMax(&s_last, tid);
-      __syncthreads();
-      if (s_pick < 0 && tid == s_last) {
-        // rounding left the draw outside every run: the last token with mass
+      for (int w = 0; w < kWalkWaves; ++w) lt = max(lt, s_lastw[w]);
+      if (tid == lt) {
         int last = -1;
-        for (int64_t j = j0; j < j1; ++j) {
+#pragma unroll
+        for (int c = 0; c < kWalkCache; ++c)
+#pragma unroll
+          for (int e = 0; e < W; ++e)
+            if (pc[c][e] > 0.f) last = (int)((j0 + c) * W + e);
+        for (int64_t j = j0 + kWalkCache; j < j1; ++j) {
           float pv[W];
           p_at(j, pv);
 #pragma unroll
           for (int e = 0; e < W; ++e)
             if (pv[e] > 0.f) last = (int)(j * W + e);
         }
-        s_pick = last;
+        s_fb = last;
       }
       __syncthreads();
-      pick = s_pick;
+      pick = s_fb;
     }
-    if (tid == 0) {
-      a.bonus_tok[b] = pick;
-      a.accept_len[b] = depth;
-    }
-    return;
+  }
+  if (tid == 0) {
+    a.bonus_tok[b] = pick;
+    a.accept_len[b] = bp.depth;
   }
 }
 
