@@ -382,7 +382,7 @@ tv_status_t tv_graft_update(int32_t* adj, int32_t vocab, int32_t k, const void* 
  *                vocab) bytes, 256-byte aligned: per-node normalisers, children
  *                and rejection steps, and per-share partial sums. Contents on
  *                entry are ignored; calls sharing it must not overlap.
- * Launches max_children + 3 kernels (every node's rejection chain is prepared
+ * Launches max_children + 2 kernels (every node's rejection chain is prepared
  * for all nodes at once, then one walk per request).
  * Decisions are taken in fp32: a uniform within rounding of its threshold may
  * go either way. On a malformed tree indices are clamped and nothing is read or

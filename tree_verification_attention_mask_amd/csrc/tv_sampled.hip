@@ -29,9 +29,10 @@
 //
 // Kernels (every node of the batch in parallel; each node's rows are cut into
 // S shares, one 256-thread workgroup each):
-//   pass 0:   share partials of both softmax normalisers; share 0 also lists
-//             the node's children (index order, tokens in the vocabulary)
-//             with their uniforms.
+//   pass 0:   share partials of both softmax normalisers; one more workgroup
+//             a row lists the node's children (index order, tokens in the
+//             vocabulary) with their uniforms, repeated tokens and both
+//             logits at each child's token.
 //   pass k:   (k = 1 .. max_children) combine the shares' partials of the pass
 //             before and fix (beta_{k-1}, gamma_{k-1}) with each share's sum of
 //             that state's residual (the partial of F over F); then, for a
@@ -72,7 +73,7 @@ struct ChildInfo {
   int32_t tok, local;  // token, request-local node index
   float P, Q, u;       // target / draft probability of the token, the child's uniform
   int32_t dup;         // earlier child with the same token, or -1
-  int32_t pad[2];
+  float xa, xb;        // target / draft logit of the token
 };
 struct Step {
   float beta, gamma;
@@ -122,35 +123,48 @@ __device__ __forceinline__ void share(int64_t units, int S, int s, int64_t& u0, 
   u1 = min(units, u0 + per);
 }
 
+// One batch of a pass sweep: units base + u * kPassThreads + thread, u <
+// kPassUnroll, of two rows, loaded from a clamped index (a thread's loads
+// are issued together; base < u1).
+template <typename T, bool VEC>
+__device__ __forceinline__ void load_batch(const T* ra, const T* rb, int64_t base, int64_t u1,
+                                           float (&ya)[kPassUnroll][VocabUnit<T, VEC>::W],
+                                           float (&yb)[kPassUnroll][VocabUnit<T, VEC>::W]) {
+  constexpr int W = VocabUnit<T, VEC>::W;
+#pragma unroll
+  for (int u = 0; u < kPassUnroll; ++u) {
+    const int64_t j = min(base + u * kPassThreads + (int64_t)threadIdx.x, u1 - 1);
+    VocabUnit<T, VEC>::load(ra + j * W, ya[u]);
+    VocabUnit<T, VEC>::load(rb + j * W, yb[u]);
+  }
+}
+// fn(ya, yb, unit, valid) over a loaded batch.
+template <int W, typename Fn>
+__device__ __forceinline__ void visit_batch(float (&ya)[kPassUnroll][W], float (&yb)[kPassUnroll][W],
+                                            int64_t base, int64_t u1, Fn&& fn) {
+#pragma unroll
+  for (int u = 0; u < kPassUnroll; ++u) {
+    const int64_t j = base + u * kPassThreads + threadIdx.x;
+    fn(ya[u], yb[u], j, j < u1);
+  }
+}
+
 // Visit the units [u0, u1) of two rows, kPassUnroll units per thread in
-// flight at once (loads from a clamped index, so that a thread's loads are
-// issued together); fn(ya, yb, unit, valid).
+// flight at once; fn(ya, yb, unit, valid).
 template <typename T, bool VEC, typename Fn>
 __device__ __forceinline__ void for_units(const T* ra, const T* rb, int64_t u0, int64_t u1, Fn&& fn) {
   constexpr int W = VocabUnit<T, VEC>::W;
   for (int64_t base = u0; base < u1; base += kPassUnroll * kPassThreads) {
     float ya[kPassUnroll][W], yb[kPassUnroll][W];
-#pragma unroll
-    for (int u = 0; u < kPassUnroll; ++u) {
-      const int64_t j = min(base + u * kPassThreads + (int64_t)threadIdx.x, u1 - 1);
-      VocabUnit<T, VEC>::load(ra + j * W, ya[u]);
-      VocabUnit<T, VEC>::load(rb + j * W, yb[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < kPassUnroll; ++u) {
-      const int64_t j = base + u * kPassThreads + threadIdx.x;
-      fn(ya[u], yb[u], j, j < u1);
-    }
+    load_batch<T, VEC>(ra, rb, base, u1, ya, yb);
+    visit_batch<W>(ya, yb, base, u1, fn);
   }
 }
 
 // Sum over a pass workgroup of two values per thread.
 __device__ float2 pass_sum2(float x, float y, float2* s_red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    x += __shfl_xor(x, off, 64);
-    y += __shfl_xor(y, off, 64);
-  }
+  x = wave_sum(x);
+  y = wave_sum(y);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) s_red[wave] = make_float2(x, y);
   __syncthreads();
@@ -168,33 +182,51 @@ template <typename T, bool VEC>
 __global__ __launch_bounds__(kPassThreads) void sampled_prep_kernel(SArgs a, const T* __restrict__ tl,
                                                                        const T* __restrict__ dl) {
   constexpr int W = VocabUnit<T, VEC>::W;
-  __shared__ MaxSum s_ms[kPassWaves];
+  __shared__ MaxSum s_ms[kPassWaves], s_mq[kPassWaves];
   __shared__ int s_cnt[kPassWaves];
+  __shared__ int32_t s_tok[TV_MAX_SAMPLED_CHILDREN], s_loc[TV_MAX_SAMPLED_CHILDREN];
   const int g = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int64_t units = a.vocab / W;  // VEC only when vocab % W == 0
-  int64_t u0, u1;
-  share(units, a.S, s, u0, u1);
   const T* ra = tl + (int64_t)g * a.vocab;
   const T* rb = dl + (int64_t)g * a.vocab;
-  MaxSum mp{-INFINITY, 0.f}, mq{-INFINITY, 0.f};
-  for_units<T, VEC>(ra, rb, u0, u1, [&](float (&ya)[W], float (&yb)[W], int64_t, bool valid) {
-    if (!valid) return;
+  if (s < a.S) {
+    // share partials of both softmax normalisers
+    const int64_t units = a.vocab / W;  // VEC only when vocab % W == 0
+    int64_t u0, u1;
+    share(units, a.S, s, u0, u1);
+    MaxSum mp{-INFINITY, 0.f}, mq{-INFINITY, 0.f};
+    for_units<T, VEC>(ra, rb, u0, u1, [&](float (&ya)[W], float (&yb)[W], int64_t, bool valid) {
+      if (!valid) return;
 #pragma unroll
-    for (int e = 0; e < W; ++e) {
-      ya[e] = nan_to_ninf(ya[e]);
-      yb[e] = nan_to_ninf(yb[e]);
+      for (int e = 0; e < W; ++e) {
+        ya[e] = nan_to_ninf(ya[e]);
+        yb[e] = nan_to_ninf(yb[e]);
+      }
+      fold(mp, ya, a.c);
+      fold(mq, yb, a.c);
+    });
+    mp = wave_merge(mp);
+    mq = wave_merge(mq);
+    if (lane == 0) {
+      s_ms[wave] = mp;
+      s_mq[wave] = mq;
     }
-    fold(mp, ya, a.c);
-    fold(mq, yb, a.c);
-  });
-  mp = block_merge<kPassWaves>(mp, s_ms);
-  mq = block_merge<kPassWaves>(mq, s_ms);
-  if (tid == 0) a.part[(size_t)g * a.S + s] = make_float4(mp.m, mp.s, mq.m, mq.s);
-  if (s != 0) return;
+    __syncthreads();
+    if (tid == 0) {
+      MaxSum rp = s_ms[0], rq = s_mq[0];
+#pragma unroll
+      for (int w = 1; w < kPassWaves; ++w) {
+        rp = merge(rp, s_ms[w]);
+        rq = merge(rq, s_mq[w]);
+      }
+      a.part[(size_t)g * a.S + s] = make_float4(rp.m, rp.s, rq.m, rq.s);
+    }
+    return;
+  }
 
-  // the node's request (cu_nodes ascending: cu[b] <= g < cu[b + 1]) and its
-  // children in index order
+  // the extra workgroup of the row: the node's request (cu_nodes ascending:
+  // cu[b] <= g < cu[b + 1]), its children in index order with their
+  // uniforms, repeated tokens and both logits at each child's token
   int lo = 0, hi = a.batch;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -207,7 +239,6 @@ __global__ __launch_bounds__(kPassThreads) void sampled_prep_kernel(SArgs a, con
   const int local = g - r0;
   int m = 0;
   if (local >= 0 && local < n) {  // (uniform; false only for malformed offsets)
-    ChildInfo* ch = a.child + (size_t)g * a.C;
     for (int base = local + 1; base < n; base += kPassThreads) {
       const int ci = base + tid;
       int x = -1;
@@ -228,20 +259,35 @@ __global__ __launch_bounds__(kPassThreads) void sampled_prep_kernel(SArgs a, con
       }
       const int pos = off + __popcll(bal & ((1ull << lane) - 1));
       if (is && pos < a.C) {
-        ChildInfo c{};
-        c.tok = x;
-        c.local = ci;
-        c.u = a.u_accept[r0 + ci];
-        c.dup = -1;
-        ch[pos] = c;
+        s_tok[pos] = x;
+        s_loc[pos] = ci;
       }
       m += tot;
       __syncthreads();
     }
   }
+  m = min(m, a.C);
+  ChildInfo* ch = a.child + (size_t)g * a.C;
+  for (int j = tid; j < m; j += kPassThreads) {
+    ChildInfo c;
+    c.tok = s_tok[j];
+    c.local = s_loc[j];
+    c.P = 0.f;
+    c.Q = 0.f;
+    c.u = a.u_accept[r0 + c.local];
+    c.dup = -1;
+    for (int i = 0; i < j; ++i)
+      if (s_tok[i] == c.tok) {
+        c.dup = i;
+        break;
+      }
+    c.xa = load_one(ra + c.tok);
+    c.xb = load_one(rb + c.tok);
+    ch[j] = c;
+  }
   if (tid == 0) {
     NodeInfo ni{};
-    ni.m = min(m, a.C);
+    ni.m = m;
     ni.next = -1;
     a.node[g] = ni;
   }
@@ -253,8 +299,11 @@ __global__ __launch_bounds__(kPassThreads) void sampled_pass_kernel(SArgs a, int
                                                                       const T* __restrict__ dl) {
   constexpr int W = VocabUnit<T, VEC>::W;
   __shared__ float2 s_red[kPassWaves];
+  __shared__ float4 s_prev[kMaxShares];
   __shared__ ChildInfo s_ch[TV_MAX_SAMPLED_CHILDREN];
   __shared__ Step s_st[TV_MAX_SAMPLED_CHILDREN];
+  __shared__ int32_t s_tin[TV_MAX_SAMPLED_CHILDREN];  // pass 1: children's tokens inside the share
+  __shared__ int s_nin;
   const int g = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const bool lead = (s == 0 && tid == 0);
@@ -265,61 +314,78 @@ __global__ __launch_bounds__(kPassThreads) void sampled_pass_kernel(SArgs a, int
   // the node's last pass fixes (beta_{m-1}, gamma_{m-1}): after it every
   // child's test is known, and share 0 takes them
   const bool tests = (s == 0 && k == last);
+  const bool sweep = k <= m;  // a share partial of F(beta_k) to take
   const int S = a.S;
   const float4* prev = a.part + (size_t)((k - 1) & 1) * a.total_nodes * S + (size_t)g * S;
   ChildInfo* ch = a.child + (size_t)g * a.C;
   Step* st = a.step + (size_t)g * (a.C + 1);
   const T* ra = tl + (int64_t)g * a.vocab;
   const T* rb = dl + (int64_t)g * a.vocab;
+  const int64_t units = a.vocab / W;
+  int64_t u0, u1;
+  share(units, S, s, u0, u1);
+
+  // the sweep's first batch is requested before the tables, so that both
+  // round trips overlap
+  float ya[kPassUnroll][W], yb[kPassUnroll][W];
+  const bool early = sweep && u0 < u1;
+  if (early) load_batch<T, VEC>(ra, rb, u0, u1, ya, yb);
+  // the tables: the pass before's share partials, the children, the steps so far
+  if (tid < S) s_prev[tid] = prev[tid];
+  for (int j = tid; j < m; j += kPassThreads) s_ch[j] = ch[j];
+  for (int l = tid; l < k - 1; l += kPassThreads) s_st[l] = st[l];
+  if (tid == 0) s_nin = 0;
+  __syncthreads();
+  // every wave combines the shares' partials itself (lane i holds share i;
+  // S <= 64): the same operations in every wave and every workgroup
+  const float4 pv = lane < S ? s_prev[lane] : make_float4(-INFINITY, 0.f, -INFINITY, 0.f);
 
   if (k == 1) {
-    // normalisers from the shares, in share order (every workgroup alike)
-    MaxSum mp{-INFINITY, 0.f}, mq{-INFINITY, 0.f};
-    for (int i = 0; i < S; ++i) {
-      const float4 p = prev[i];
-      mp = merge(mp, MaxSum{p.x, p.y});
-      mq = merge(mq, MaxSum{p.z, p.w});
-    }
+    // normalisers from the shares, in share order (every workgroup alike),
+    // then the probabilities of the children's tokens
+    const MaxSum mp = wave_merge(MaxSum{pv.x, pv.y});
+    const MaxSum mq = wave_merge(MaxSum{pv.z, pv.w});
     ni.lp = mp.m + __log2f(mp.s);
     ni.lq = mq.m + __log2f(mq.s);
-  } else if (k == 2) {
-    float snc = 0.f;
-    for (int i = 0; i < S; ++i) snc += prev[i].y;
-    ni.snc = snc;
-  }
-  // the children: pass 1 fills in the probabilities of their tokens and the
-  // repeated tokens, later passes read them
-  for (int j = tid; j < m; j += kPassThreads) {
-    ChildInfo c = ch[j];
-    if (k == 1) {
-      c.P = prob(load_one(ra + c.tok), a.c, ni.lp);
-      c.Q = prob(load_one(rb + c.tok), a.c, ni.lq);
-      c.dup = -1;
-      for (int i = 0; i < j; ++i)
-        if (ch[i].tok == c.tok) {
-          c.dup = i;
-          break;
-        }
+    for (int j = tid; j < m; j += kPassThreads) {
+      const int t = s_ch[j].tok;
+      if (t >= u0 * W && t < u1 * W) s_tin[atomicAdd(&s_nin, 1)] = t;
+      const float P = prob(s_ch[j].xa, a.c, ni.lp);
+      const float Q = prob(s_ch[j].xb, a.c, ni.lq);
+      s_ch[j].P = P;
+      s_ch[j].Q = Q;
+      if (s == 0) {
+        ch[j].P = P;
+        ch[j].Q = Q;
+      }
     }
-    s_ch[j] = c;
+    __syncthreads();
+  } else if (k == 2) {
+    ni.snc = wave_sum(lane < S ? pv.y : 0.f);
   }
-  if (tests)
-    for (int l = tid; l < k - 1; l += kPassThreads) s_st[l] = st[l];
-  __syncthreads();
-  if (s == 0 && k == 1)
-    for (int j = tid; j < m; j += kPassThreads) ch[j] = s_ch[j];
   if (lead && k <= 2) a.node[g] = ni;
 
   // (beta_{k-1}, gamma_{k-1})
   Step cur{0.f, 1.f};
   float F = 0.f;
   if (k >= 2) {
-    const Step pk = st[k - 2];
+    const Step pk = s_st[k - 2];
     const float beta = pk.beta + pk.gamma * inv_mass(ni.snc, s_ch, m, k - 2);
-    for (int i = 0; i < S; ++i) F += prev[i].x;
+    F = wave_sum(lane < S ? pv.x : 0.f);
     cur = (F > 0.f) ? Step{beta, F} : pk;
   }
   if (lead) st[k - 1] = cur;
+  // this share's sum of the state's residual max(0, P - beta Q) / gamma, kept
+  // for the walk's bonus draw when a node's last step leaves p unchanged
+  if (tid == 0) {
+    float* bs = a.bonus + (size_t)g * S + s;
+    if (k == 1) {
+      const float4 p0 = s_prev[s];  // this share's (max, sum) of the target's exponents
+      *bs = (p0.x == -INFINITY) ? 0.f : p0.y * __builtin_amdgcn_exp2f(p0.x - ni.lp);
+    } else if (F > 0.f) {
+      *bs = s_prev[s].x / F;
+    }
+  }
   if (tests) {
     // the children's tests, one lane each (a test depends on no earlier
     // outcome, only on the state its child meets); the first that passes
@@ -352,26 +418,13 @@ __global__ __launch_bounds__(kPassThreads) void sampled_pass_kernel(SArgs a, int
       if (lane == 0) a.node[g].next = first;
     }
   }
-  // this share's sum of the state's residual max(0, P - beta Q) / gamma, kept
-  // for the walk's bonus draw when a node's last step leaves p unchanged
-  if (tid == 0) {
-    float* bs = a.bonus + (size_t)g * S + s;
-    if (k == 1) {
-      const float4 p0 = prev[s];  // this share's (max, sum) of the target's exponents
-      *bs = (p0.x == -INFINITY) ? 0.f : p0.y * __builtin_amdgcn_exp2f(p0.x - ni.lp);
-    } else if (F > 0.f) {
-      *bs = prev[s].x / F;
-    }
-  }
 
-  const int64_t units = a.vocab / W;
-  int64_t u0, u1;
-  share(units, S, s, u0, u1);
-  if (k <= m) {
+  if (sweep) {
     // share partial of F(beta_k); pass 1 also the draft mass outside the children
     const float beta = cur.beta + cur.gamma * inv_mass(ni.snc, s_ch, m, k - 1);
+    const int nin = (k == 1) ? s_nin : 0;
     float f = 0.f, snc = 0.f;
-    for_units<T, VEC>(ra, rb, u0, u1, [&](float (&ya)[W], float (&yb)[W], int64_t j, bool valid) {
+    auto visit = [&](float (&ya)[W], float (&yb)[W], int64_t j, bool valid) {
       if (!valid) return;
       float Q[W];
 #pragma unroll
@@ -384,7 +437,7 @@ __global__ __launch_bounds__(kPassThreads) void sampled_pass_kernel(SArgs a, int
         // draft mass outside the children's tokens: a unit holding none of
         // them adds all its values, else value by value
         bool hit = false;
-        for (int i = 0; i < m; ++i) hit |= (s_ch[i].tok / W == j);
+        for (int i = 0; i < nin; ++i) hit |= (s_tin[i] / W == j);
         if (!hit) {
 #pragma unroll
           for (int e = 0; e < W; ++e) snc += Q[e];
@@ -393,40 +446,21 @@ __global__ __launch_bounds__(kPassThreads) void sampled_pass_kernel(SArgs a, int
           for (int e = 0; e < W; ++e) {
             const int v = (int)(j * W + e);
             bool child = false;
-            for (int i = 0; i < m; ++i) child |= (s_ch[i].tok == v);
+            for (int i = 0; i < nin; ++i) child |= (s_tin[i] == v);
             snc += child ? 0.f : Q[e];
           }
         }
       }
-    });
+    };
+    if (early) {
+      visit_batch<W>(ya, yb, u0, u1, visit);
+      for_units<T, VEC>(ra, rb, u0 + kPassUnroll * kPassThreads, u1, visit);
+    }
     const float2 r = pass_sum2(f, snc, s_red);
     if (tid == 0)
       a.part[(size_t)(k & 1) * a.total_nodes * S + (size_t)g * S + s] = make_float4(r.x, r.y, 0.f, 0.f);
   }
 }
-
-// The value of the lane that DPP control CTRL names, 0 where there is none
-// (a shift past the row's or the wave's edge, or a row ROWS leaves out).
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_in(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, false));
-}
-
-// Inclusive prefix sum over a wave in lane order: shifts by 1, 2, 4, 8 inside
-// each row of 16 lanes, then the last lane of a row added into the next rows
-// (row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3).
-__device__ __forceinline__ float wave_incl_sum(float x) {
-  x += dpp_in<0x111, 0xf>(x);
-  x += dpp_in<0x112, 0xf>(x);
-  x += dpp_in<0x114, 0xf>(x);
-  x += dpp_in<0x118, 0xf>(x);
-  x += dpp_in<0x142, 0xa>(x);
-  x += dpp_in<0x143, 0xc>(x);
-  return x;
-}
-
-// The previous lane's value (wave_shr:1), 0 in lane 0.
-__device__ __forceinline__ float wave_prev(float x) { return dpp_in<0x138, 0xf>(x); }
 
 // Inclusive prefix sum over the walk block of one value per thread, in thread
 // order; returns the thread's inclusive sum, the block total and, in `excl`,
@@ -579,13 +613,13 @@ __global__ __launch_bounds__(kWalkThreads) void sampled_walk_kernel(SArgs a, int
     if (m >= 1) {
       const Step pk = s_st[m - 1];
       const float beta = pk.beta + pk.gamma * inv_mass(ni.snc, s_ch, m, m - 1);
-      Fm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_incl_sum(pm)), 63));
+      Fm = wave_sum(pm);
       fin = (Fm > 0.f) ? Step{beta, Fm} : pk;
     }
     const float si = lane < S ? ((Fm > 0.f) ? pm / Fm : s_share[lane]) : 0.f;
     const float incl = wave_incl_sum(si);
     const float excl = wave_prev(incl);
-    const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
+    const float total = lane_value(incl, 63);
     const float target = ub * total;
     const uint64_t in = __ballot(excl <= target && target < incl);
     const uint64_t mass = __ballot(si > 0.f);
@@ -593,7 +627,7 @@ __global__ __launch_bounds__(kWalkThreads) void sampled_walk_kernel(SArgs a, int
     float t = INFINITY;
     if (in != 0) {
       sh = __ffsll((unsigned long long)in) - 1;
-      t = target - __int_as_float(__builtin_amdgcn_readlane(__float_as_int(excl), sh));
+      t = target - lane_value(excl, sh);
     } else if (mass != 0) {  // at or past the total: the last token with mass
       sh = 63 - __clzll((unsigned long long)mass);
     }
@@ -744,7 +778,9 @@ hipError_t run_sampled(const SArgs& a, const void* tl, const void* dl, hipStream
   const T* d = static_cast<const T*>(dl);
   if (a.total_nodes > 0) {
     const dim3 grid(a.total_nodes, a.S);
-    hipLaunchKernelGGL((sampled_prep_kernel<T, VEC>), grid, dim3(kPassThreads), 0, stream, a, t, d);
+    // one more workgroup a row in pass 0 lists the node's children
+    hipLaunchKernelGGL((sampled_prep_kernel<T, VEC>), dim3(a.total_nodes, a.S + 1), dim3(kPassThreads), 0,
+                       stream, a, t, d);
     for (int k = 1; k <= a.C; ++k)
       hipLaunchKernelGGL((sampled_pass_kernel<T, VEC>), grid, dim3(kPassThreads), 0, stream, a, k,
                          t, d);

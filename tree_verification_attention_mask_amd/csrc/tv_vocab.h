@@ -75,6 +75,51 @@ __device__ __forceinline__ void fold(MaxSum& r, const float (&x)[N], float c) {
   r = MaxSum{m, acc};
 }
 
+// Wave-wide DPP helpers (64 lanes, no LDS round trip). dpp_from: the value
+// of the lane that DPP control CTRL names, `old` where there is none (a
+// shift past the row's or the wave's edge, or a row ROWS leaves out).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_from(float old, float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), CTRL, ROWS, 0xf, false));
+}
+// Inclusive prefix sum in lane order: shifts by 1, 2, 4, 8 inside each row of
+// 16 lanes, then a row's last lane added into the rows after it (row_bcast:15
+// into rows 1 and 3, row_bcast:31 into rows 2 and 3).
+__device__ __forceinline__ float wave_incl_sum(float x) {
+  x += dpp_from<0x111, 0xf>(0.f, x);
+  x += dpp_from<0x112, 0xf>(0.f, x);
+  x += dpp_from<0x114, 0xf>(0.f, x);
+  x += dpp_from<0x118, 0xf>(0.f, x);
+  x += dpp_from<0x142, 0xa>(0.f, x);
+  x += dpp_from<0x143, 0xc>(0.f, x);
+  return x;
+}
+// The previous lane's value (wave_shr:1), 0 in lane 0.
+__device__ __forceinline__ float wave_prev(float x) { return dpp_from<0x138, 0xf>(0.f, x); }
+__device__ __forceinline__ float lane_value(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+// Sum and maximum over the wave, the same value in every lane.
+__device__ __forceinline__ float wave_sum(float x) { return lane_value(wave_incl_sum(x), 63); }
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_from<0x111, 0xf>(x, x));
+  x = fmaxf(x, dpp_from<0x112, 0xf>(x, x));
+  x = fmaxf(x, dpp_from<0x114, 0xf>(x, x));
+  x = fmaxf(x, dpp_from<0x118, 0xf>(x, x));
+  x = fmaxf(x, dpp_from<0x142, 0xa>(x, x));
+  x = fmaxf(x, dpp_from<0x143, 0xc>(x, x));
+  return lane_value(x, 63);
+}
+// (max, sum) merge over the wave: the maximum, then every lane's sum
+// rescaled to it and added up (-inf maxima add nothing).
+__device__ __forceinline__ MaxSum wave_merge(MaxSum v) {
+  const float m = wave_max(v.m);
+  if (m == -INFINITY) return MaxSum{m, 0.f};
+  const float t = (v.m == -INFINITY) ? 0.f : v.s * __builtin_amdgcn_exp2f(v.m - m);
+  return MaxSum{m, wave_sum(t)};
+}
+
 // Block-wide merge of one value per thread over NW waves; every thread gets
 // the result. s_red holds NW entries; the trailing barrier lets the next call
 // reuse it.
