@@ -37,16 +37,19 @@
 //             before and fix (beta_{k-1}, gamma_{k-1}) with each share's sum of
 //             that state's residual (the partial of F over F); then, for a
 //             node with m >= k children, share partials of F(beta_k) (pass 1
-//             also the draft mass outside the children's tokens).
-//   walk:     one 1024-thread workgroup per request: at each node one parallel
-//             read of its children and steps, the tests in order with scalar
-//             arithmetic every thread repeats; at the last node it fixes the
-//             final step from the last pass's partials, finds the share that
-//             holds the bonus draw from the share sums and inverts the CDF
-//             inside it (per-thread runs in token order, a block scan, then a
-//             rescan of the one run). The bonus distribution after the last
-//             step needs no sweep of its own: its share sums are the last
-//             F partials over F.
+//             also the draft mass outside the children's tokens). A node's
+//             last pass (k = max(m, 1)) knows the state every child meets and
+//             takes all the children's tests at once (one lane each: a test
+//             depends on no earlier outcome), storing the first that passes.
+//   walk:     one 1024-thread workgroup per request: its tables copied into
+//             LDS in one round trip, the first wave follows the stored
+//             accepted child level by level; at the last node it fixes the
+//             final step from the last pass's partials and finds, with a wave
+//             scan of the share sums, the share that holds the bonus draw;
+//             the block inverts the CDF inside it (per-thread runs in token
+//             order, a block scan, then a rescan of the one run). The bonus
+//             distribution after the last step needs no sweep of its own: its
+//             share sums are the last F partials over F.
 #include "tv_launch.h"
 #include "tv_vocab.h"
 
