@@ -122,8 +122,21 @@ def cpu_baseline(w, seconds):
     return {"value": reps * w.total_nodes / el, "unit": "tree-tokens/s", "cores": 1,
             "kind": "oracle",
             "sample": "%d whole steps of %s (mask + fp64 attention over all %d x %d rows + "
-                      "acceptance) in %.1f s, one thread" % (reps, w.name, w.total_nodes,
-                                                             w.num_q_heads, el)}
+                      "acceptance) in %.1f s, one thread of %s (%d in this process's "
+                      "affinity set)" % (reps, w.name, w.total_nodes, w.num_q_heads, el,
+                                         cpu_model(), len(os.sched_getaffinity(0)))}
+
+
+def cpu_model():
+    """The host CPU's model name (for the CPU baseline's record)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 def main():
