@@ -288,9 +288,9 @@ void attn_bf16_kernel(Params p) {
   // Q fragments (B operand of S^T): lane (r16, q4) holds row r16 of its
   // subtile, d = 32s + 8q4 .. +7. Subtiles st = wave + NW r hold rows
   // row0 + 16 st ..; the first nv of them (a wave-uniform count) have a real
-  // row. Padding rows carry zero Q and are never stored, so the MFMAs below
-  // run unguarded. These loads, and the mask rows', stay in flight while the
-  // first K/V tiles are requested.
+  // row. Padding rows carry the request's first row's Q and are never
+  // stored, so the MFMAs below run unguarded. These loads, and the mask
+  // rows', stay in flight while the first K/V tiles are requested.
   int nv = 0;
 #pragma unroll
   for (int r = 0; r < RW; ++r) nv += (row0 + 16 * (wave + NW * r) < rows) ? 1 : 0;
@@ -311,23 +311,25 @@ void attn_bf16_kernel(Params p) {
     rloc[r] = i;
     rnode[r] = n0 + i;
     orow[r] = (n0 + i) * p.hq + g * G + hl;
-    // unconditional loads (a padding row reads the request's first row and
-    // drops it): a per-lane branch here would wait for each load in turn
+    // unconditional loads whose values are first used after the first tiles
+    // are requested: a padding row reads the request's first row (its scores
+    // are computed, never stored, and no other row depends on them; its mask
+    // is never consulted), and no select on the loaded values here, which
+    // would wait for them before the tile requests. With one mask word the
+    // second load reads the first again; bits past the last node are cut by
+    // the request's key range.
     m_w0[r] = 0ull; m_w1[r] = 0ull;
     if (anchor) {
-      const uint64_t a = (uint64_t)(uint32_t)p.mask.anchor_pos[rnode[r]] |
-                         ((uint64_t)(uint32_t)p.mask.branch_depth[rnode[r]] << 32);
-      m_w0[r] = row_ok[r] ? a : 0ull;
+      m_w0[r] = (uint64_t)(uint32_t)p.mask.anchor_pos[rnode[r]] |
+                ((uint64_t)(uint32_t)p.mask.branch_depth[rnode[r]] << 32);
     } else if (bits_in_regs) {
-      const uint64_t w0 = p.mask.bits[(size_t)rnode[r] * p.mask.words];
-      const uint64_t w1 = p.mask.bits[(size_t)rnode[r] * p.mask.words + (p.mask.words - 1)];
-      m_w0[r] = row_ok[r] ? w0 : 0ull;
-      m_w1[r] = (row_ok[r] && p.mask.words == 2) ? w1 : 0ull;
+      m_w0[r] = p.mask.bits[(size_t)rnode[r] * p.mask.words];
+      m_w1[r] = p.mask.bits[(size_t)rnode[r] * p.mask.words + (p.mask.words - 1)];
     }
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
       const uint4 u = *reinterpret_cast<const uint4*>(p.q + (size_t)orow[r] * D + 32 * s + 8 * q4);
-      qf[r][s] = row_ok[r] ? __builtin_bit_cast(bf16x8, u) : bf16x8{};
+      qf[r][s] = __builtin_bit_cast(bf16x8, u);
     }
   }
   // Visibility of keys [k0, k0 + 64) for this lane's row of subtile r.
