@@ -575,9 +575,17 @@ void attn_bf16_kernel(Params p) {
   // for P = 0 to contribute nothing); the next barrier publishes them
   auto zero_tail = [&](int stage, int k0) {
     if (k0 + kTile <= kv_end) return;
-    for (int e = tid; e < TILE_E; e += T) {
-      const int key = 16 * (e / (16 * D)) + (e & 15);  // element (group, d, key%16)
-      if (k0 + key >= kv_end) sV[stage][e] = static_cast<__bf16>(0.f);
+    const int lim = kv_end - k0;  // tile keys >= lim are past the end
+    // 16-byte chunks: 8 consecutive keys of one d (layout [group][d][16 keys])
+    for (int c = tid; c < TILE_E / 8; c += T) {
+      const int e = 8 * c;
+      const int key0 = 16 * (e / (16 * D)) + (e & 15);
+      if (key0 + 7 < lim) continue;
+      bf16x8* ch = reinterpret_cast<bf16x8*>(&sV[stage][e]);
+      bf16x8 v = *ch;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (key0 + i >= lim) ? static_cast<__bf16>(0.f) : v[i];
+      *ch = v;
     }
     __builtin_amdgcn_s_waitcnt(W_ALL & ~0x0F00);  // lgkmcnt(0): zeros written
   };
@@ -626,7 +634,8 @@ void attn_bf16_kernel(Params p) {
   int c_prev = ke;  // tile m-1 (none yet)
   int c_n1 = next_tile(c_cur), c_n2 = next_tile(c_n1);
   // V of stage STAGES-1 is read (times P = 0) by the first M cluster
-  for (int e = tid; e < TILE_E; e += T) sV[STAGES - 1][e] = static_cast<__bf16>(0.f);
+  for (int c = tid; c < TILE_E / 8; c += T)
+    reinterpret_cast<uint4*>(&sV[STAGES - 1][0])[c] = uint4{0u, 0u, 0u, 0u};
   // the page list and the zeros are written; make them visible (Q and mask
   // loads stay in flight)
   __builtin_amdgcn_s_waitcnt(W_ALL & ~0x0F00);
