@@ -187,14 +187,35 @@ void attn_bf16_kernel(Params p) {
       s_len[i] = max(p.prefix_len[i], 0) + clampi(p.cu_nodes[i + 1], c0, p.total_nodes) - c0;
     }
     __syncthreads();
-    for (int i = tid; i < p.batch; i += T) {
-      const int li = s_len[i];
-      int rank = 0;
-      for (int j = 0; j < p.batch; ++j) {
-        const int lj = s_len[j];
-        rank += (lj > li || (lj == li && j < i)) ? 1 : 0;
+    if (p.batch <= T / 8) {
+      // eight lanes per request (batch <= 64), each counting the requests
+      // ranked ahead of it among eight others; the counts are added across
+      // the eight lanes
+      const int i = tid >> 3, part = tid & 7;
+      int cnt = 0;
+      if (i < p.batch) {
+        const int li = s_len[i];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int j = part * 8 + q;
+          const int lj = j < p.batch ? s_len[j] : -1;
+          cnt += (lj > li || (lj == li && j < i)) ? 1 : 0;
+        }
       }
-      s_order[rank] = i;
+      cnt += __shfl_xor(cnt, 1, 8);
+      cnt += __shfl_xor(cnt, 2, 8);
+      cnt += __shfl_xor(cnt, 4, 8);
+      if (i < p.batch && part == 0) s_order[cnt] = i;
+    } else {
+      for (int i = tid; i < p.batch; i += T) {
+        const int li = s_len[i];
+        int rank = 0;
+        for (int j = 0; j < p.batch; ++j) {
+          const int lj = s_len[j];
+          rank += (lj > li || (lj == li && j < i)) ? 1 : 0;
+        }
+        s_order[rank] = i;
+      }
     }
     __syncthreads();
     b = s_order[b];
