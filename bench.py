@@ -127,6 +127,48 @@ def cpu_baseline(w, seconds):
                                          cpu_model(), len(os.sched_getaffinity(0)))}
 
 
+def cpu_baseline_threads(w, seconds):
+    """The same oracle over whole steps, the attention rows split into equal
+    parts over host threads (one part each; the C routine runs outside the
+    interpreter lock), at most 16 threads and no more than the affinity set."""
+    import numpy as np
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    q = w.q.float().numpy()
+    k = w.k_cache.float().numpy()
+    v = w.v_cache.float().numpy()
+    rows = np.stack(np.meshgrid(np.arange(w.total_nodes), np.arange(w.num_q_heads),
+                                indexing="ij"), -1).reshape(-1, 2).astype(np.int32)
+    parts = [c for c in np.array_split(rows, threads) if len(c)]
+
+    def part(c):
+        oracle.tree_attn(q, k, v, w.block_table, w.prefix_len, w.cu_nodes, w.parent,
+                         w.num_q_heads, w.num_kv_heads, w.scale, rows=c)
+
+    reps = 0
+    with ThreadPoolExecutor(len(parts)) as ex:
+        t0 = time.perf_counter()
+        while True:
+            if w.mask_kind == "bits":
+                oracle.mask_bits(w.parent, w.cu_nodes, w.words_per_node)
+            else:
+                oracle.mask_anchor(w.parent, w.cu_nodes)
+            list(ex.map(part, parts))
+            if w.draft_tok is not None:
+                oracle.accept(w.parent, w.draft_tok, w.target_tok, w.cu_nodes, w.max_depth)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return {"value": reps * w.total_nodes / el, "unit": "tree-tokens/s", "cores": len(parts),
+            "kind": "oracle",
+            "sample": "%d whole steps of %s in %.1f s, the %d x %d attention rows in %d equal "
+                      "parts on %d threads of %s (%d in this process's affinity set)"
+                      % (reps, w.name, el, w.total_nodes, w.num_q_heads, len(parts), len(parts),
+                         cpu_model(), len(os.sched_getaffinity(0)))}
+
+
 def cpu_model():
     """The host CPU's model name (for the CPU baseline's record)."""
     try:
@@ -274,6 +316,21 @@ def main():
     ms_total = ev0.elapsed_time(ev1)
     ms_per_step = ms_total / args.steps
     log("timed %d steps: %.3f ms (events), %.3f s wall" % (args.steps, ms_total, wall))
+
+    # spread over replays: each replay of the R-step graph timed on its own
+    # (after the timed region, which it does not touch)
+    per_replay = []
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(max(10, min(reps_full, 200)))]
+    for a_, b_ in evs:
+        a_.record()
+        g_full.replay()
+        b_.record()
+    torch.cuda.synchronize()
+    per_replay = np.array([a_.elapsed_time(b_) * 1e3 / R for a_, b_ in evs])
+    spread = {"unit": "us per step, mean of one replay of %d steps" % R,
+              "replays": len(evs), "p10": float(np.percentile(per_replay, 10)),
+              "median": float(np.median(per_replay)), "p90": float(np.percentile(per_replay, 90))}
 
     def time_graph(g, calls_per_replay):
         reps = max(1, args.steps // R)
@@ -423,12 +480,15 @@ def main():
                  "algorithmic_flops_per_launch": alg_flops},
         "breakdown_us": {"tree_mask_build": us_mask, "tree_verify_attn": us_attn,
                          "tree_accept": us_acc, "step": ms_per_step * 1e3},
+        "step_spread_us": spread,
     }
     if next_rows:
         result["next_rows"] = next_rows
     if not args.no_cpu_baseline:
         log("timing the CPU oracle (about %.0f s)" % args.cpu_seconds)
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        log("timing the CPU oracle on host threads (about %.0f s)" % args.cpu_seconds)
+        result["cpu_baseline_threads"] = cpu_baseline_threads(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
