@@ -169,14 +169,21 @@ void attn_bf16_kernel(Params p) {
 
   // block order: split fastest, then kv head, then request, row block
   // slowest and last first -- later row blocks see more tree keys (causal
-  // trunks), so the longest workgroups of every head start first
+  // trunks), so the longest workgroups of every head start first (with the
+  // snake below, which keeps the four CU groups of an XCD evenly loaded)
   int wg = blockIdx.x;
   const int split = wg % p.splits;
   wg /= p.splits;
   const int g = wg % p.hkv;
   wg /= p.hkv;
   int b = wg % p.batch;
-  const int rb = p.row_blocks - 1 - wg / p.batch;
+  // Dispatch position t of the row block (0 first): last row blocks first,
+  // every other full group of four in reverse ("snake"), so that workgroups
+  // dealt out in turn over four groups of CUs give each group a like share
+  // of long and short blocks.
+  int t = wg / p.batch;
+  if (((t >> 2) & 1) && (t | 3) < p.row_blocks) t ^= 3;
+  const int rb = p.row_blocks - 1 - t;
   if (p.lpt) {
     // Longest-first: when the grid takes several rounds of the CUs, blocks
     // of long requests are dispatched first (ranked by key count, ties by
