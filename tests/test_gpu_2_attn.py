@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import tree_verification_attention_mask_amd as tv
 import workloads as W
 from tv_testlib import Dev, assert_attn_close, oracle_attn
@@ -209,3 +210,40 @@ def test_status_codes():
                                  ctypes.c_float(0.088), ctypes.byref(ms), out.data_ptr(), None,
                                  None, 0, None)
     assert st == 2   # head_dim 96 unsupported
+
+
+def test_prefix_beyond_one_split_page_list_many_requests():
+    """Maximum-size edge: a 65,500-key prefix holds more pages than one key
+    split's page list (4096 pages of 16 tokens), so the keys are split even
+    though the grid already covers the CUs; 513 single-node requests are more
+    than the in-kernel longest-first ranking takes (256). Every request's pages
+    come from a 64-page pool; a seeded sample of rows is recomputed by the
+    oracle."""
+    rng = np.random.default_rng(513)
+    batch, hq, hkv, d, page, pool, prefix = 513, 32, 8, 128, 16, 64, 65500
+    pages_per = (prefix + 1 + page - 1) // page
+    q = torch.from_numpy(rng.standard_normal((batch, hq, d)).astype(np.float32)).to(torch.bfloat16)
+    k = torch.from_numpy(rng.standard_normal((pool, hkv, page, d)).astype(np.float32)).to(torch.bfloat16)
+    v = torch.from_numpy(rng.standard_normal((pool, hkv, d, page)).astype(np.float32)).to(torch.bfloat16)
+    table = rng.integers(0, pool, size=(batch, pages_per)).astype(np.int32)
+    prefix_len = np.full(batch, prefix, np.int32)
+    cu = np.arange(batch + 1, dtype=np.int32)
+    parent = np.full(batch, -1, np.int32)
+    assert tv.verify_attn_workspace_size(batch, batch, 1, prefix, hq, hkv, d, torch.bfloat16) > 0
+    dev = "cuda"
+    dq, dk, dv = q.to(dev), k.to(dev), v.to(dev)
+    dt, dp, dc = (torch.from_numpy(x).to(dev) for x in (table, prefix_len, cu))
+    m = tv.tree_mask_build(torch.from_numpy(parent).to(dev), dc, 1, kind="bits")
+    print("long prefix, many requests: batch", batch, "prefix", prefix, flush=True)
+    out, lse = tv.tree_verify_attn(dq, dk, dv, dt, dp, dc, m, 1, prefix, scale=d ** -0.5)
+    torch.cuda.synchronize()
+    rows = {(0, 0), (batch - 1, hq - 1)}
+    while len(rows) < 24:
+        rows.add((int(rng.integers(batch)), int(rng.integers(hq))))
+    rows = np.array(sorted(rows), np.int32)
+    ref, rlse = oracle.tree_attn(q, k, v, table, prefix_len, cu, parent, hq, hkv, d ** -0.5,
+                                 rows=rows)
+    got = out[rows[:, 0], rows[:, 1]].float().cpu().numpy()
+    gl = lse[rows[:, 0], rows[:, 1]].cpu().numpy()
+    print(assert_attn_close(got, ref, "bf16", gl, rlse, what="long prefix, many requests"))
+    assert torch.isfinite(out.float()).all()
