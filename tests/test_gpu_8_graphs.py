@@ -1,4 +1,4 @@
-"""HIP-graph replays of the multi-launch entry points (stochastic acceptance,
+"""HIP-graph replays of a whole verification step and of the multi-launch entry points (stochastic acceptance,
 the Graft update, E2E-TV statistics): every replay, with eager work and
 synchronisations between replays, must give the eager result bit for bit
 (the library records no memset, and every scratch table is rewritten before
@@ -96,3 +96,46 @@ def test_e2e_tv_graph_replays():
     def call():
         outs["r"] = tv.e2e_tv_stats(t, d, cu, 1.0)
     _replays(call, lambda: list(outs["r"]), eager)
+
+
+_STEP_WORKLOADS = {
+    "graft-tree-11-splits": lambda: W.make(2),
+    "ragged-batch-longest-first": lambda: W.make(3, batch=40, prefix_range=(50, 700)),
+    "anchor-trunk-and-branches": lambda: W.make(5, trunk=512, n_anchors=8, anchor_lo=64),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_STEP_WORKLOADS))
+def test_verify_step_graph_replays(name):
+    """One step (mask build, attention, acceptance) captured in a HIP graph:
+    every replay, after its outputs were overwritten and eager work ran, gives
+    the eager step's results bit for bit (the split merge, the longest-first
+    order and the anchor-form mask included)."""
+    from tv_testlib import Dev
+    w = _STEP_WORKLOADS[name]()
+    d = Dev(w)
+    res = {}
+
+    def step():
+        m = d.mask()
+        out, lse = d.attn(mask=m)
+        res.update(out=out, lse=lse, depth=m["depth"], err=m["err"])
+        if d.draft is not None:
+            al, path, bonus = d.accept()
+            res.update(accept_len=al, path=path, bonus=bonus)
+
+    step()
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in res.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        for v in res.values():
+            v.fill_(float("nan") if v.is_floating_point() else -7)
+        junk = torch.randn(1 << 20, device="cuda") * i   # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in eager.items():
+            assert torch.equal(res[k], v), (name, k, i)
+        del junk
