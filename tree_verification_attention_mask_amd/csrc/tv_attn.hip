@@ -627,6 +627,9 @@ void attn_bf16_kernel(Params p) {
   // the V stage it reads was zeroed; after the last, the scores are unused.
   auto cluster_m = [&](int m) {
     if (nv == 0) return;
+    // the wave in its MFMA cluster issues first on its SIMD; the other
+    // group's VALU cluster fills the matrix core's busy cycles
+    __builtin_amdgcn_s_setprio(1);
     pv((m - 1) & (STAGES - 1), pf);
     qk(m & (STAGES - 1), sc);
     // software pipeline of the cluster: LDS fragment reads run kAhead
@@ -641,6 +644,7 @@ void attn_bf16_kernel(Params p) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, RW * kAhead, 0);
+    __builtin_amdgcn_s_setprio(0);
   };
   auto cluster_v = [&](int k0) {
     if (nv == 0) return;
