@@ -130,6 +130,35 @@ def test_mask_anchor_specopd_tree():
     np.testing.assert_array_equal(depth, odepth)
 
 
+def test_mask_anchor_request_sizes_around_the_staged_limit():
+    """ANCHOR requests of up to 8192 nodes are read into LDS at once; exactly
+    8192 nodes (trunk 8128 + 4 branches of 16) and, with a larger max_nodes,
+    8660 nodes (trunk 8500 + 10 branches of 16, the strided kernel) match the
+    oracle; a request past 8192 nodes under a max_nodes of 8192 (the caller
+    understating it) is reported malformed while its neighbour is exact."""
+    rng = np.random.default_rng(8192)
+    t8192 = W.trunk_branch_tree(8128, np.sort(rng.integers(0, 8128, size=4)).tolist(), 16)
+    t8660 = W.trunk_branch_tree(8500, np.sort(rng.integers(0, 8500, size=10)).tolist(), 16)
+    small = W.trunk_branch_tree(40, [3, 17, 17], 5)
+    assert len(t8192) == 8192 and len(t8660) == 8660
+    for trees, max_nodes in (([t8192, small], 8192), ([small, t8660, t8192], 8660)):
+        par, cu = _pack(trees)
+        ap, bd, depth, err = _gpu_anchor(par, cu, max_nodes)
+        oap, obd, odepth, oerr = oracle.mask_anchor(par, cu)
+        assert err.tolist() == oerr.tolist() == [0] * len(trees)
+        np.testing.assert_array_equal(ap, oap)
+        np.testing.assert_array_equal(bd, obd)
+        np.testing.assert_array_equal(depth, odepth)
+    par, cu = _pack([t8660, small])
+    ap, bd, depth, err = _gpu_anchor(par, cu, 8192)
+    oap, obd, odepth, oerr = oracle.mask_anchor(par, cu)
+    assert err.tolist() == [1, 0]
+    assert (ap[:8660] == -1).all() and (bd[:8660] == 0).all() and (depth[:8660] == -1).all()
+    np.testing.assert_array_equal(ap[8660:], oap[8660:])
+    np.testing.assert_array_equal(bd[8660:], obd[8660:])
+    np.testing.assert_array_equal(depth[8660:], odepth[8660:])
+
+
 # -------------------------------------------------------------- acceptance --
 
 def _check_accept(w, max_depth=None):

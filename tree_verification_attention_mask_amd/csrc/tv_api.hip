@@ -38,8 +38,8 @@ extern "C" tv_status_t tv_tree_mask_build(const int32_t* parent, const int32_t* 
   }
   if (kind == TV_MASK_ANCHOR) {
     if (!anchor_pos || !branch_depth) return TV_ERR_INVALID_ARGUMENT;
-    return launched(launch_mask_anchor(parent, cu_nodes, batch, total_nodes, anchor_pos,
-                                       branch_depth, depth, err, stream));
+    return launched(launch_mask_anchor(parent, cu_nodes, batch, total_nodes, max_nodes,
+                                       anchor_pos, branch_depth, depth, err, stream));
   }
   return TV_ERR_INVALID_ARGUMENT;
 }

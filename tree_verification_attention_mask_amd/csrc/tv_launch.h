@@ -10,8 +10,9 @@ hipError_t launch_mask_bits(const int32_t* parent, const int32_t* cu_nodes, int3
                             int32_t total_nodes, int32_t words, uint64_t* bits, int32_t* depth,
                             int32_t* err, hipStream_t stream);
 hipError_t launch_mask_anchor(const int32_t* parent, const int32_t* cu_nodes, int32_t batch,
-                              int32_t total_nodes, int32_t* anchor_pos, int32_t* branch_depth,
-                              int32_t* depth, int32_t* err, hipStream_t stream);
+                              int32_t total_nodes, int32_t max_nodes, int32_t* anchor_pos,
+                              int32_t* branch_depth, int32_t* depth, int32_t* err,
+                              hipStream_t stream);
 hipError_t launch_accept(const int32_t* parent, const int32_t* draft_tok, const int32_t* target_tok,
                          const int32_t* cu_nodes, int32_t batch, int32_t total_nodes,
                          int32_t max_nodes, int32_t max_depth, int32_t* accept_len, int32_t* path,

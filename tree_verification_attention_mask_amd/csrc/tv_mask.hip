@@ -228,6 +228,123 @@ __global__ __launch_bounds__(kMaskThreads) void mask_anchor_kernel(
   if (threadIdx.x == 0) err[b] = 0;
 }
 
+// The same ANCHOR-form decision for requests of at most kAnchorCap nodes
+// (the host's max_nodes): the request's parent array is read into LDS at once
+// (every thread's loads in flight together) and each thread then handles a
+// contiguous run of kAnchorPerThread nodes, so validation, the trunk length,
+// the shape check and the branch-start scan cost one memory round trip, not
+// one per strided pass; the outputs are written in the strided order. A
+// request past kAnchorCap nodes (more than max_nodes allows) is reported
+// malformed.
+constexpr int kAnchorThreads = 1024;
+constexpr int kAnchorPerThread = 8;
+constexpr int kAnchorCap = kAnchorThreads * kAnchorPerThread;
+
+__global__ __launch_bounds__(kAnchorThreads) void mask_anchor_small_kernel(
+    const int32_t* __restrict__ parent, const int32_t* __restrict__ cu_nodes, int32_t total_nodes,
+    int32_t* __restrict__ anchor_pos, int32_t* __restrict__ branch_depth,
+    int32_t* __restrict__ depth, int32_t* __restrict__ err) {
+  __shared__ int s_par[kAnchorCap];
+  __shared__ int s_start[kAnchorCap];  // branch start of each branch node
+  __shared__ int s_incl[kAnchorThreads];
+  __shared__ int s_wave[kAnchorThreads / 64];
+  __shared__ int s_trunk;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int n0 = clampi(cu_nodes[b], 0, total_nodes);
+  const int n = clampi(cu_nodes[b + 1], n0, total_nodes) - n0;
+  const int32_t* par = parent + n0;
+  const int m = min(n, kAnchorCap);
+  int pv[kAnchorPerThread];
+#pragma unroll
+  for (int j = 0; j < kAnchorPerThread; ++j) {
+    const int i = tid + j * kAnchorThreads;
+    pv[j] = i < m ? par[i] : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < kAnchorPerThread; ++j) {
+    const int i = tid + j * kAnchorThreads;
+    if (i < m) s_par[i] = pv[j];
+  }
+  if (tid == 0) s_trunk = n;
+  __syncthreads();
+  // this thread's run [i0, i0 + kAnchorPerThread): parent validity, and the
+  // first k >= 1 whose parent is not k - 1 (the trunk length T, else n)
+  const int i0 = tid * kAnchorPerThread;
+  int bad = 0, tk = n;
+#pragma unroll
+  for (int j = 0; j < kAnchorPerThread; ++j) {
+    const int i = i0 + j;
+    if (i < m) {
+      const int p = s_par[i];
+      bad |= (i == 0) ? (p != -1) : (p < 0 || p >= i);
+      if (i >= 1 && p != i - 1) tk = min(tk, i);
+    }
+  }
+  if (tk < n) atomicMin(&s_trunk, tk);
+  int e = (__syncthreads_or(bad) || n <= 0 || n > kAnchorCap) ? 1 : 0;
+  const int T = s_trunk;
+  // every node past the trunk starts a branch (parent < T) or continues the
+  // previous node's branch (parent == i - 1)
+  int shape_bad = 0;
+  if (!e) {
+#pragma unroll
+    for (int j = 0; j < kAnchorPerThread; ++j) {
+      const int i = i0 + j;
+      if (i >= T && i < n) {
+        const int p = s_par[i];
+        shape_bad |= !(p < T || p == i - 1);
+      }
+    }
+  }
+  if (__syncthreads_or(shape_bad) && !e) e = 2;
+  if (e) {
+    for (int i = tid; i < n; i += kAnchorThreads) {
+      anchor_pos[n0 + i] = -1;
+      branch_depth[n0 + i] = 0;
+      depth[n0 + i] = -1;
+    }
+    if (tid == 0) err[b] = e;
+    return;
+  }
+  // branch start of node i = the latest s <= i with parent[s] < T: a running
+  // max of (i if it starts a branch, else -1), within the run and then over
+  // the runs of earlier threads
+  int run = -1;
+#pragma unroll
+  for (int j = 0; j < kAnchorPerThread; ++j) {
+    const int i = i0 + j;
+    if (i >= T && i < n && s_par[i] < T) run = i;
+  }
+  s_incl[tid] = block_scan_max(run, s_wave);
+  __syncthreads();
+  // each branch node's start into LDS, then the outputs in the strided
+  // order (consecutive threads, consecutive nodes: whole cache lines)
+  int st = tid > 0 ? s_incl[tid - 1] : -1;
+#pragma unroll
+  for (int j = 0; j < kAnchorPerThread; ++j) {
+    const int i = i0 + j;
+    if (i >= T && i < n) {
+      if (s_par[i] < T) st = i;
+      s_start[i] = st;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += kAnchorThreads) {
+    if (i < T) {
+      anchor_pos[n0 + i] = i;
+      branch_depth[n0 + i] = 0;
+      depth[n0 + i] = i;
+    } else {
+      const int s = s_start[i];
+      const int a = s_par[s];
+      anchor_pos[n0 + i] = a;
+      branch_depth[n0 + i] = i - s + 1;
+      depth[n0 + i] = a + 1 + (i - s);
+    }
+  }
+  if (tid == 0) err[b] = 0;
+}
+
 }  // namespace
 
 hipError_t launch_mask_bits(const int32_t* parent, const int32_t* cu_nodes, int32_t batch,
@@ -255,10 +372,15 @@ hipError_t launch_mask_bits(const int32_t* parent, const int32_t* cu_nodes, int3
 }
 
 hipError_t launch_mask_anchor(const int32_t* parent, const int32_t* cu_nodes, int32_t batch,
-                              int32_t total_nodes, int32_t* anchor_pos, int32_t* branch_depth,
-                              int32_t* depth, int32_t* err, hipStream_t stream) {
-  hipLaunchKernelGGL(mask_anchor_kernel, dim3(batch), dim3(kMaskThreads), 0, stream, parent,
-                     cu_nodes, total_nodes, anchor_pos, branch_depth, depth, err);
+                              int32_t total_nodes, int32_t max_nodes, int32_t* anchor_pos,
+                              int32_t* branch_depth, int32_t* depth, int32_t* err,
+                              hipStream_t stream) {
+  if (max_nodes <= kAnchorCap)
+    hipLaunchKernelGGL(mask_anchor_small_kernel, dim3(batch), dim3(kAnchorThreads), 0, stream,
+                       parent, cu_nodes, total_nodes, anchor_pos, branch_depth, depth, err);
+  else
+    hipLaunchKernelGGL(mask_anchor_kernel, dim3(batch), dim3(kMaskThreads), 0, stream, parent,
+                       cu_nodes, total_nodes, anchor_pos, branch_depth, depth, err);
   return hipGetLastError();
 }
 
