@@ -120,7 +120,8 @@ typedef struct {
  *                 branch (parent = i-1).
  *   depth         out [total_nodes]  number of ancestors (root 0)
  *   err           out [batch]  0 = ok; 1 = malformed parent[] (parent[0] != -1, or a
- *                 parent outside [0, i)) or, BITS, more nodes than words_per_node*64;
+ *                 parent outside [0, i)) or, BITS, more nodes than words_per_node*64, or,
+ *                 ANCHOR with max_nodes <= 8192, a request of more than 8192 nodes;
  *                 2 = ANCHOR form impossible for this tree. A request with err != 0 gets
  *                 an all-zero mask (ANCHOR: anchor_pos -1, branch_depth 0) and depth -1.
  * Unused outputs of the other form may be NULL.
