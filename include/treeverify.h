@@ -166,7 +166,8 @@ size_t tv_tree_verify_attn_workspace_size(int32_t batch, int32_t total_nodes, in
  *   v_cache      [num_pages][num_kv_heads][head_dim][page_size]  dtype (d-major pages:
  *                the page_size keys of one (kv head, d) are contiguous)
  *   num_pages    (host) pages in the caches; page ids are clamped into range
- *   block_table  [batch][max_pages_per_req]  entries past a request's last page are not read
+ *   block_table  [batch][max_pages_per_req]  entries past a request's last page may hold any
+ *                value (never used for a key); page ids outside [0, num_pages) are clamped
  *   prefix_len   [batch]
  *   cu_nodes     [batch + 1]
  *   max_prefix_len (host) >= every prefix_len

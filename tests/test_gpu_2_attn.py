@@ -247,3 +247,40 @@ def test_prefix_beyond_one_split_page_list_many_requests():
     gl = lse[rows[:, 0], rows[:, 1]].cpu().numpy()
     print(assert_attn_close(got, ref, "bf16", gl, rlse, what="long prefix, many requests"))
     assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_block_table_garbage_and_out_of_range_pages(dtype):
+    """Block-table entries past a request's last page may hold anything (they
+    are never used for a key): garbage there leaves the output bit-identical.
+    Page ids outside [0, num_pages) inside the used range are clamped: the
+    output equals, bit for bit, the one with those ids written clamped."""
+    rng = np.random.default_rng(77)
+    trees = [W.random_tree(rng, 30, max_children=3), W.random_tree(rng, 9)]
+    w = W.build_workload("table", trees, [300, 41], 8, 2, 128, dtype, rng, permute_pages=True,
+                         spare_pages=6, tokens=False)
+    d = Dev(w)
+    m = d.mask()
+    last = (w.prefix_len + w.nodes_per_request - 1) // w.page_size   # each request's last page
+    base = np.zeros((w.batch, w.block_table.shape[1] + 8), np.int32)  # 8 more entries a row
+    base[:, :w.block_table.shape[1]] = w.block_table
+    d.table = torch.from_numpy(base).cuda()
+    ref_out, ref_lse = d.attn(mask=m)
+    junk = base.copy()
+    for b in range(w.batch):
+        tail = junk[b, last[b] + 1:]
+        tail[:] = rng.choice([-(1 << 30), -1, w.num_pages, w.num_pages + 9, 1 << 30], size=tail.shape)
+    d.table = torch.from_numpy(junk).cuda()
+    o1, l1 = d.attn(mask=m)
+    assert torch.equal(o1, ref_out) and torch.equal(l1, ref_lse)
+    # out-of-range ids inside the used range, and the same ids written clamped
+    bad = base.copy()
+    bad[0, 2], bad[0, 5], bad[1, 0] = w.num_pages + 7, -3, 1 << 29
+    clamped = bad.copy()
+    clamped[0, 2], clamped[0, 5], clamped[1, 0] = w.num_pages - 1, 0, w.num_pages - 1
+    d.table = torch.from_numpy(bad).cuda()
+    o2, l2 = d.attn(mask=m)
+    d.table = torch.from_numpy(clamped).cuda()
+    o3, l3 = d.attn(mask=m)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o3) and torch.equal(l2, l3)
