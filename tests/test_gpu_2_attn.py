@@ -284,3 +284,21 @@ def test_block_table_garbage_and_out_of_range_pages(dtype):
     o3, l3 = d.attn(mask=m)
     torch.cuda.synchronize()
     assert torch.equal(o2, o3) and torch.equal(l2, l3)
+
+
+@pytest.mark.parametrize("layout", ["first", "middle", "last", "several"])
+def test_empty_requests_in_batch(layout):
+    """Requests with no tree nodes (their mask reports err 1; they own no
+    rows) beside ragged ones: the other requests' rows match the oracle, with
+    the keys split (five splits of a 300-key prefix) and merged."""
+    rng = np.random.default_rng(len(layout))
+    a, b = W.random_tree(rng, 20, max_children=3), W.random_tree(rng, 7)
+    trees, prefix = {"first": ([[], a, b], [40, 100, 300]),
+                     "middle": ([a, [], b], [100, 50, 300]),
+                     "last": ([a, b, []], [100, 300, 7]),
+                     "several": ([[], a, [], b, []], [3, 100, 0, 300, 64])}[layout]
+    w = W.build_workload("empty " + layout, trees, prefix, 8, 2, 128, "bf16", rng,
+                         permute_pages=True, spare_pages=2, tokens=False)
+    d, out, lse = _run_and_check(w, "empty requests, " + layout)
+    err = d.mask()["err"].cpu().numpy()
+    assert err.tolist() == [0 if len(t) else 1 for t in trees]

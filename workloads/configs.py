@@ -203,7 +203,7 @@ def build_workload(name: str, trees: Sequence[Sequence[int]], prefix_len: Sequen
     cu[1:] = np.cumsum(sizes)
     parent = np.concatenate([np.asarray(t, np.int32) for t in trees]) if batch else np.zeros(0, np.int32)
     depths = [_depths(t) for t in trees]
-    max_depth = int(max(int(d.max()) for d in depths)) if batch else 0
+    max_depth = int(max((int(d.max()) if d.size else 0) for d in depths)) if batch else 0
 
     draft = target = None
     if tokens:
