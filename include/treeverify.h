@@ -134,12 +134,36 @@ tv_status_t tv_tree_mask_build(const int32_t* parent, const int32_t* cu_nodes, i
 
 /*
  * Workspace bytes tv_tree_verify_attn needs for these host shape scalars
- * (split-KV partial results). 0 means no workspace is needed.
+ * (split-KV partial results). 0 means no workspace is needed. The launch plan
+ * aims at one workgroup per compute unit of the CURRENT device (256 if HIP
+ * cannot report the count), so query with the device current that the call
+ * will run on.
  */
 size_t tv_tree_verify_attn_workspace_size(int32_t batch, int32_t total_nodes, int32_t max_nodes,
                                           int32_t max_prefix_len, int32_t num_q_heads,
                                           int32_t num_kv_heads, int32_t head_dim,
                                           int32_t dtype);
+
+/*
+ * Launch plan of tv_tree_verify_attn (host only, nothing is enqueued): how the
+ * rows of one kv head are cut into blocks and its keys into splits, and the
+ * workspace the split partials take. A pure function of the host scalars and
+ * num_cus, the compute-unit count to plan for (0 = the current device's).
+ * Returns TV_ERR_INVALID_ARGUMENT / TV_ERR_UNSUPPORTED like tv_tree_verify_attn
+ * for shapes it would reject.
+ */
+typedef struct {
+  int32_t num_cus;         /* compute units planned for */
+  int32_t rows_per_block;  /* (node, query head) rows of one kv head per workgroup */
+  int32_t row_blocks;      /* row blocks per (request, kv head) */
+  int32_t splits;          /* key splits (1: no merge) */
+  int32_t keys_per_split;  /* keys per split, a multiple of 64 */
+  size_t workspace_bytes;  /* = tv_tree_verify_attn_workspace_size for this num_cus */
+} tv_attn_plan_t;
+tv_status_t tv_tree_verify_attn_plan(int32_t batch, int32_t total_nodes, int32_t max_nodes,
+                                     int32_t max_prefix_len, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                                     int32_t num_cus, tv_attn_plan_t* plan);
 
 /*
  * tv_tree_verify_attn -- one target attention layer over the flattened tree.
@@ -216,6 +240,7 @@ tv_status_t tv_tree_verify_attn(const void* q, const void* k_cache, const void* 
  *   path         out [batch][max_depth + 1]  local node ids root..best, then -1;
  *                entries past max_depth are not written
  *   bonus_tok    out [batch]  target_tok[best] (the target's next token), or NULL
+ * A request with no nodes has no root: accept_len 0, path all -1, bonus_tok -1.
  * parent[] must be a valid tree (tv_tree_mask_build reports it); on a malformed
  * tree indices are clamped, results are undefined and nothing is read or
  * written out of bounds.

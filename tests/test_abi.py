@@ -47,6 +47,55 @@ def test_workspace_size_is_a_pure_host_query():
     assert ws(0, 60, 60, 2048, 32, 8, 128, 1) == 0         # invalid shape -> 0
 
 
+# (batch, total_nodes, max_nodes, max_prefix_len, hq, hkv) of the measured workloads
+PLAN_SHAPES = {"graft-60node-p2048": (1, 60, 60, 2048, 32, 8),
+               "dcut-b64-chains": (64, 512, 16, 4096, 32, 8),
+               "long-32k-b8-60node": (8, 480, 60, 32768, 64, 8),
+               "specopd-trunk4096-32x16": (1, 4608, 4608, 0, 32, 8)}
+
+
+@pytest.mark.parametrize("cus", [80, 256, 304])
+@pytest.mark.parametrize("shape", sorted(PLAN_SHAPES))
+def test_attention_plan_follows_the_compute_unit_count(cus, shape):
+    """The split count aims at one workgroup per compute unit of the device
+    the plan is made for; the splits cover every key; the workspace holds
+    the split partials (bf16 o + fp32 m, l per row and split) and is 0
+    without splits."""
+    batch, total, maxn, maxp, hq, hkv = PLAN_SHAPES[shape]
+    pl = tv.verify_attn_plan(batch, total, maxn, maxp, hq, hkv, 128, binding.torch.bfloat16, cus)
+    assert pl["num_cus"] == cus
+    keys = maxp + maxn
+    tiles = -(-keys // 64)
+    g = hq // hkv
+    assert pl["keys_per_split"] % 64 == 0
+    assert pl["splits"] * pl["keys_per_split"] >= keys
+    assert (pl["splits"] - 1) * pl["keys_per_split"] < keys       # no empty split
+    assert pl["row_blocks"] * pl["rows_per_block"] >= maxn * g
+    base = batch * hkv * pl["row_blocks"]
+    assert base * pl["splits"] <= max(cus, base), "more workgroups than one pass needs"
+    tps = pl["keys_per_split"] // 64
+    if base < cus and tps > 1:
+        # one tile fewer per split would need more workgroups than one pass
+        assert base * -(-tiles // (tps - 1)) > cus
+    if pl["splits"] == 1:
+        assert pl["workspace_bytes"] == 0
+    else:
+        rows = total * hq
+        o = -(-pl["splits"] * rows * 128 * 2 // 256) * 256
+        ml = -(-pl["splits"] * rows * 8 // 256) * 256
+        assert pl["workspace_bytes"] >= o + ml
+    # the workspace query plans for the current device (no GPU here: 256)
+    if cus == 256:
+        assert binding.verify_attn_workspace_size(batch, total, maxn, maxp, hq, hkv, 128,
+                                                  binding.torch.bfloat16) == pl["workspace_bytes"]
+
+
+def test_attention_plan_splits_grow_with_the_compute_units():
+    s = [tv.verify_attn_plan(1, 60, 60, 2048, 32, 8, 128, binding.torch.bfloat16, c)["splits"]
+         for c in (80, 256, 304)]
+    assert s[0] < s[1] <= s[2]
+
+
 def _attn(lib, **over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, pages=10, table=FAKE, maxp=4, prefix=FAKE, cu=FAKE, batch=1,
              total=60, maxn=60, maxP=2048, hq=32, hkv=8, d=128, page=16, dtype=1, scale=0.08,

@@ -23,5 +23,6 @@ from .binding import (  # noqa: F401
     tree_accept_sampled_workspace_size,
     tree_mask_build,
     tree_verify_attn,
+    verify_attn_plan,
     verify_attn_workspace_size,
 )

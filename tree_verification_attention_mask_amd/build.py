@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(PKG, "_build")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIB_DIR, "libtreeverify.so")
-SOURCES = ["tv_api.hip", "tv_mask.hip", "tv_accept.hip", "tv_attn.hip", "tv_dcut.hip", "tv_e2etv.hip",
+SOURCES = ["tv_api.hip", "tv_device.hip", "tv_mask.hip", "tv_accept.hip", "tv_attn.hip", "tv_dcut.hip", "tv_e2etv.hip",
            "tv_graft.hip", "tv_sampled.hip"]
 ARCH = "gfx950"
 

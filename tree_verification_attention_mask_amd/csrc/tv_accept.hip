@@ -98,14 +98,10 @@ hipError_t launch_accept(const int32_t* parent, const int32_t* draft_tok, const 
                          int32_t* bonus_tok, hipStream_t stream) {
   const int cap = max_nodes < 1 ? 1 : max_nodes;
   const size_t lds = 3 * sizeof(int32_t) * (size_t)cap;
-  static bool lds_raised = false;  // allow > 64 KiB dynamic LDS for the largest trees
-  if (!lds_raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&accept_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(3 * sizeof(int32_t) * TV_MAX_ACCEPT_NODES));
-    if (e != hipSuccess) return e;
-    lds_raised = true;
-  }
+  // allow > 64 KiB dynamic LDS for the largest trees
+  hipError_t e = raise_dynamic_lds(reinterpret_cast<const void*>(&accept_kernel),
+                                   (int)(3 * sizeof(int32_t) * TV_MAX_ACCEPT_NODES));
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(accept_kernel, dim3(batch), dim3(64), lds, stream, parent, draft_tok,
                      target_tok, cu_nodes, total_nodes, cap, max_depth, accept_len, path,
                      bonus_tok);

@@ -8,6 +8,12 @@ using namespace tv;
 
 namespace {
 inline tv_status_t launched(hipError_t e) { return e == hipSuccess ? TV_OK : TV_ERR_HIP; }
+// the attention plan aims at one workgroup per compute unit of the current
+// device; MI355X's 256 when HIP cannot report the count
+inline int32_t plan_cus() {
+  const int n = device_cu_count();
+  return n > 0 ? n : 256;
+}
 }  // namespace
 
 extern "C" const char* tv_status_string(tv_status_t s) {
@@ -52,7 +58,29 @@ extern "C" size_t tv_tree_verify_attn_workspace_size(int32_t batch, int32_t tota
       num_kv_heads < 1)
     return 0;
   return plan_attn(batch, total_nodes, max_nodes, max_prefix_len, num_q_heads, num_kv_heads,
-                   head_dim, dtype).workspace;
+                   head_dim, dtype, plan_cus()).workspace;
+}
+
+extern "C" tv_status_t tv_tree_verify_attn_plan(int32_t batch, int32_t total_nodes,
+                                                int32_t max_nodes, int32_t max_prefix_len,
+                                                int32_t num_q_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t dtype, int32_t num_cus,
+                                                tv_attn_plan_t* plan) {
+  if (!plan) return TV_ERR_INVALID_ARGUMENT;
+  if (batch < 1 || total_nodes < 1 || max_nodes < 1 || max_prefix_len < 0 || num_q_heads < 1 ||
+      num_kv_heads < 1 || num_q_heads % num_kv_heads || num_cus < 0)
+    return TV_ERR_INVALID_ARGUMENT;
+  if (dtype != TV_F32 && dtype != TV_BF16) return TV_ERR_INVALID_ARGUMENT;
+  if (head_dim != 64 && head_dim != 128) return TV_ERR_UNSUPPORTED;
+  const AttnPlan p = plan_attn(batch, total_nodes, max_nodes, max_prefix_len, num_q_heads,
+                               num_kv_heads, head_dim, dtype, num_cus > 0 ? num_cus : plan_cus());
+  plan->num_cus = p.num_cus;
+  plan->rows_per_block = dtype == TV_F32 ? 16 : 16 * p.waves * p.rw;
+  plan->row_blocks = p.row_blocks;
+  plan->splits = p.splits;
+  plan->keys_per_split = p.keys_per_split;
+  plan->workspace_bytes = p.workspace;
+  return TV_OK;
 }
 
 extern "C" tv_status_t tv_tree_verify_attn(
@@ -87,7 +115,7 @@ extern "C" tv_status_t tv_tree_verify_attn(
     return TV_ERR_INVALID_ARGUMENT;
   }
   const AttnPlan plan = plan_attn(batch, total_nodes, max_nodes, max_prefix_len, num_q_heads,
-                                  num_kv_heads, head_dim, dtype);
+                                  num_kv_heads, head_dim, dtype, plan_cus());
   if ((int64_t)batch * num_kv_heads * plan.row_blocks * plan.splits >= (int64_t(1) << 31))
     return TV_ERR_UNSUPPORTED;
   if (plan.workspace > 0) {

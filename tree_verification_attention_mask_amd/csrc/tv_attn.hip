@@ -50,7 +50,6 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kTile = 64;     // keys per tile
-constexpr int kNumCUs = 256;  // MI355X compute units (the launch plan targets one pass over them)
 constexpr int kMaxSplitPages = 4096;  // page ids one workgroup can stage (16-token pages: 64K keys)
 constexpr int kMaxLptBatch = 256;   // requests the in-kernel longest-first order handles
 constexpr float kLazyMax = 8.f;      // running-max slack before O is rescaled (log2 units)
@@ -137,8 +136,9 @@ __device__ __forceinline__ void lds_dma16(const void* src, const void* lds) {
 }
 
 template <int D, int NW, int RW, bool WIDE>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 1 : 2)))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bf16_kernel(Params p) {
+  static_assert(NW == 8, "two groups of four waves (one wave of each per SIMD)");
   constexpr int T = 64 * NW;           // threads
   constexpr int DS = D / 32;           // 32-wide d steps of S^T = K Q^T
   constexpr int DU = D / 16;           // 16-wide d subtiles of O^T
@@ -151,7 +151,7 @@ void attn_bf16_kernel(Params p) {
   constexpr int IPW = INS / NW;        // ... per wave
   constexpr int RPI = 512 / D;         // K rows per load (1 KB / row bytes)
   constexpr int VPG = D / 32;          // V loads per 16-key group (32 d rows each)
-  constexpr int GPW = (NW == 8) ? 1 : 2;  // 16-key groups one wave loads per tile
+  constexpr int GPW = 1;               // 16-key groups one wave loads per tile
   constexpr int PPT = kMaxSplitPages / T;  // page-table entries per thread
   static_assert(INS % NW == 0 && IPW * RPI == 16 * GPW && IPW == VPG * GPW, "load split");
   // Ring of STAGES tiles: K as [key][d] with 16-byte chunks XOR-swizzled by
@@ -617,7 +617,7 @@ void attn_bf16_kernel(Params p) {
     }
     __builtin_amdgcn_s_waitcnt(W_ALL & ~0x0F00);  // lgkmcnt(0): zeros written
   };
-  const bool grp_b = (NW == 8) && wave >= NW / 2;
+  const bool grp_b = wave >= NW / 2;
   f32x4 sc[RW][4];
   bf16x8 pf[RW][2];
 #pragma unroll
@@ -677,7 +677,7 @@ void attn_bf16_kernel(Params p) {
   // slot 2m ends. Tiles are then requested three ahead, in slot 2m+1, into
   // that stage (3 tiles in flight instead of 2: these blocks are bound by
   // HBM latency, not by the matrix cores).
-  const bool solo = (NW == 4) || (rows - row0 <= 16 * (NW / 2));
+  const bool solo = rows - row0 <= 16 * (NW / 2);
   int c_n3 = solo ? next_tile(c_n2) : ke;  // tile to request in slot 2m+1 (solo)
   int pgn[GPW];
   if (c_cur < ke) { pages_for(c_cur, pgn); issue(0, c_cur, pgn); }
@@ -972,7 +972,6 @@ hipError_t run_bf16(const Params& prm, int grid, hipStream_t stream) {
 
 template <int D>
 hipError_t dispatch_bf16(const Params& prm, const AttnPlan& plan, int grid, hipStream_t stream) {
-  if (plan.waves == 4) return run_bf16<D, 4, 1>(prm, grid, stream);
   if (plan.rw == 1) return run_bf16<D, 8, 1>(prm, grid, stream);
   return run_bf16<D, 8, 2>(prm, grid, stream);
 }
@@ -980,8 +979,9 @@ hipError_t dispatch_bf16(const Params& prm, const AttnPlan& plan, int grid, hipS
 }  // namespace
 
 AttnPlan plan_attn(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_prefix_len,
-                   int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype) {
+                   int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype, int32_t num_cus) {
   AttnPlan pl{};
+  pl.num_cus = num_cus > 0 ? num_cus : 1;
   const long G = hkv > 0 ? hq / hkv : 1;
   const long rows = (long)max_nodes * G;
   if (dtype == TV_F32) {
@@ -1005,7 +1005,7 @@ AttnPlan plan_attn(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_
   const long base = (long)batch * hkv * pl.row_blocks;
   // One 128 KB-LDS workgroup fits a CU: cut the keys into splits until the
   // workgroups cover the CUs once; more splits only add partial traffic.
-  const long cus = kNumCUs;
+  const long cus = pl.num_cus;
   long splits = std::max(1L, std::min(tiles, cus / base));
   // a split's pages must fit the block's LDS page list (16-token pages)
   const long max_tps = (long)(kMaxSplitPages - 8) * 16 / kTile;
@@ -1081,7 +1081,7 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t stre
   p.keys_per_split = plan.keys_per_split;
   p.scale_log2 = a.scale * kLog2e;
   const int grid = a.batch * a.hkv * plan.row_blocks * plan.splits;
-  p.lpt = (a.batch >= 2 && a.batch <= kMaxLptBatch && grid > kNumCUs) ? 1 : 0;
+  p.lpt = (a.batch >= 2 && a.batch <= kMaxLptBatch && grid > plan.num_cus) ? 1 : 0;
   hipError_t e = (a.head_dim == 64) ? dispatch_bf16<64>(p, plan, grid, stream)
                                     : dispatch_bf16<128>(p, plan, grid, stream);
   if (e != hipSuccess || plan.splits == 1) return e;

@@ -193,14 +193,10 @@ hipError_t launch_dcut_select(const float* conf, const int32_t* tokens, int32_t 
                               int32_t draft_len, int32_t budget, int32_t* n_keep,
                               int32_t* cu_nodes, int32_t* parent, int32_t* packed_tokens,
                               hipStream_t stream) {
-  static bool lds_raised = false;  // the score array may exceed 64 KiB
-  if (!lds_raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dcut_select_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(TV_MAX_DCUT_DRAFT_POSITIONS * sizeof(uint32_t)));
-    if (e != hipSuccess) return e;
-    lds_raised = true;
-  }
+  // the score array may exceed 64 KiB
+  hipError_t e = raise_dynamic_lds(reinterpret_cast<const void*>(&dcut_select_kernel),
+                                   (int)(TV_MAX_DCUT_DRAFT_POSITIONS * sizeof(uint32_t)));
+  if (e != hipSuccess) return e;
   const size_t lds = (size_t)batch * draft_len * sizeof(uint32_t);
   hipLaunchKernelGGL(dcut_select_kernel, dim3(1), dim3(kDcutThreads), lds, stream, conf, tokens,
                      batch, draft_len, budget, n_keep, cu_nodes, parent, packed_tokens);

@@ -81,15 +81,18 @@ struct AttnArgs {
 // Launch plan of the bf16 path: rows per block, key splits. A pure function
 // of host scalars, shared by the workspace query and the launch.
 struct AttnPlan {
-  int waves;           // wavefronts per workgroup (4 or 8)
+  int num_cus;         // compute units the plan was made for
+  int waves;           // wavefronts per workgroup (8)
   int rw;              // 16-row subtiles per wave (block rows = 16 * waves * rw)
   int row_blocks;      // blocks over the node*group rows of one kv head
   int splits;          // key splits
   int keys_per_split;  // multiple of 64
   size_t workspace;    // bytes of split partials (0 when splits == 1)
 };
+// num_cus: compute units of the device the call runs on (the split count
+// aims at one workgroup per compute unit).
 AttnPlan plan_attn(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_t max_prefix_len,
-                   int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype);
+                   int32_t hq, int32_t hkv, int32_t head_dim, int32_t dtype, int32_t num_cus);
 // returns the launch's hipError_t
 hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream);
 

@@ -6,6 +6,12 @@
 
 namespace tv {
 
+// Compute units of the current device (cached per device; 0 if HIP cannot say).
+int device_cu_count();
+// hipFuncSetAttribute(kernel, MaxDynamicSharedMemorySize, bytes) once per
+// (current device, kernel); later calls return hipSuccess at once.
+hipError_t raise_dynamic_lds(const void* kernel, int bytes);
+
 hipError_t launch_mask_bits(const int32_t* parent, const int32_t* cu_nodes, int32_t batch,
                             int32_t total_nodes, int32_t words, uint64_t* bits, int32_t* depth,
                             int32_t* err, hipStream_t stream);

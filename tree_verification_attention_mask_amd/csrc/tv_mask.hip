@@ -358,14 +358,10 @@ hipError_t launch_mask_bits(const int32_t* parent, const int32_t* cu_nodes, int3
   }
   const size_t cap = 64 * (size_t)words;
   const size_t lds = cap * words * sizeof(uint64_t) + cap * sizeof(int32_t);
-  static bool lds_raised = false;  // allow > 64 KiB dynamic LDS (words > 11)
-  if (!lds_raised) {
-    const size_t max_lds = 64 * TV_MAX_MASK_WORDS * (TV_MAX_MASK_WORDS * sizeof(uint64_t) + sizeof(int32_t));
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mask_bits_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_lds);
-    if (e != hipSuccess) return e;
-    lds_raised = true;
-  }
+  // allow > 64 KiB dynamic LDS (words > 11)
+  const size_t max_lds = 64 * TV_MAX_MASK_WORDS * (TV_MAX_MASK_WORDS * sizeof(uint64_t) + sizeof(int32_t));
+  hipError_t e = raise_dynamic_lds(reinterpret_cast<const void*>(&mask_bits_kernel), (int)max_lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mask_bits_kernel, dim3(batch), dim3(kMaskThreads), lds, stream, parent,
                      cu_nodes, total_nodes, words, bits, depth, err);
   return hipGetLastError();
