@@ -2,13 +2,17 @@
 
 Argument marshalling only: tensors become device pointers, host scalars are
 passed through, outputs are allocated with torch when the caller does not
-supply them, and every call is enqueued on torch's current HIP stream.  All
-computation happens in the library's kernels.  There is no fallback: if the
+supply them, and every call is enqueued on torch's current HIP stream (or on
+the ``stream`` argument: the call then runs with that stream current, so its
+temporaries are allocated and freed in that stream's order, after the stream
+has been made to wait for the current one).  All computation happens in the
+library's kernels.  There is no fallback: if the
 library is missing or a call fails, an exception is raised.
 """
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch
@@ -23,7 +27,8 @@ MAX_MASK_WORDS = 16
 MAX_ACCEPT_NODES = 8192
 
 # every symbol the header declares
-EXPORTS = ("tv_tree_mask_build", "tv_tree_verify_attn_workspace_size", "tv_tree_verify_attn",
+EXPORTS = ("tv_tree_mask_build", "tv_tree_verify_attn_workspace_size", "tv_tree_verify_attn_plan",
+           "tv_tree_verify_attn",
            "tv_tree_accept", "tv_dcut_select", "tv_e2e_tv_stats", "tv_graft_retrieve",
            "tv_graft_update_workspace_size", "tv_graft_update",
            "tv_tree_accept_sampled_workspace_size", "tv_tree_accept_sampled", "tv_status_string")
@@ -34,6 +39,12 @@ class TVError(RuntimeError):
     def __init__(self, fn: str, status: int, msg: str):
         super().__init__("%s failed: status %d (%s)" % (fn, status, msg))
         self.status = status
+
+
+class AttnPlan(ctypes.Structure):
+    _fields_ = [("num_cus", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
+                ("row_blocks", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("keys_per_split", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class Mask(ctypes.Structure):
@@ -59,6 +70,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tv_tree_mask_build.restype = ctypes.c_int
     lib.tv_tree_verify_attn_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
     lib.tv_tree_verify_attn_workspace_size.restype = S
+    lib.tv_tree_verify_attn_plan.argtypes = [I, I, I, I, I, I, I, I, I, ctypes.POINTER(AttnPlan)]
+    lib.tv_tree_verify_attn_plan.restype = ctypes.c_int
     lib.tv_tree_verify_attn.argtypes = [P, P, P, I, P, I, P, P, I, I, I, I, I, I, I, I, I,
                                         ctypes.c_float, ctypes.POINTER(Mask), P, P, P, S, P]
     lib.tv_tree_verify_attn.restype = ctypes.c_int
@@ -103,14 +116,35 @@ def _dev_i32(x, device):
     return torch.as_tensor(x, dtype=torch.int32, device=device).contiguous()
 
 
-def _stream(stream):
+def _stream(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run ``fn`` with its ``stream`` keyword argument as the current stream.
+
+    The stream first waits for the caller's current stream (the inputs were
+    made there); temporaries ``fn`` allocates then belong to ``stream``, so
+    the caching allocator does not hand their memory out again before the
+    kernels enqueued on ``stream`` have run.
+    """
+    @functools.wraps(fn)
+    def run(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, **kw)
+        cur = torch.cuda.current_stream(stream.device)
+        if stream == cur:
+            return fn(*args, **kw)
+        stream.wait_stream(cur)
+        with torch.cuda.stream(stream):
+            return fn(*args, **kw)
+    return run
+
+
+@_on_stream
 def tree_mask_build(parent: torch.Tensor, cu_nodes: torch.Tensor, max_nodes: int,
-                    kind: str = "bits", words_per_node: int | None = None, out: dict | None = None,
-                    stream=None) -> dict:
+                    kind: str = "bits", words_per_node: int | None = None, out: dict | None = None) -> dict:
     """Depth and ancestor mask of every node (``tv_tree_mask_build``).
 
     Returns a dict with ``kind``, ``depth``, ``err`` and either ``bits``
@@ -123,17 +157,22 @@ def tree_mask_build(parent: torch.Tensor, cu_nodes: torch.Tensor, max_nodes: int
     k = TV_MASK_BITS if kind == "bits" else TV_MASK_ANCHOR
     words = words_per_node if words_per_node is not None else max(1, (max_nodes + 63) // 64)
     o = dict(out or {})
-    o.setdefault("depth", torch.empty(n, dtype=torch.int32, device=dev))
-    o.setdefault("err", torch.empty(batch, dtype=torch.int32, device=dev))
+    if "depth" not in o:
+        o["depth"] = torch.empty(n, dtype=torch.int32, device=dev)
+    if "err" not in o:
+        o["err"] = torch.empty(batch, dtype=torch.int32, device=dev)
     if k == TV_MASK_BITS:
-        o.setdefault("bits", torch.empty((n, words), dtype=torch.int64, device=dev))
+        if "bits" not in o:
+            o["bits"] = torch.empty((n, words), dtype=torch.int64, device=dev)
     else:
-        o.setdefault("anchor_pos", torch.empty(n, dtype=torch.int32, device=dev))
-        o.setdefault("branch_depth", torch.empty(n, dtype=torch.int32, device=dev))
+        if "anchor_pos" not in o:
+            o["anchor_pos"] = torch.empty(n, dtype=torch.int32, device=dev)
+        if "branch_depth" not in o:
+            o["branch_depth"] = torch.empty(n, dtype=torch.int32, device=dev)
     st = lib.tv_tree_mask_build(_ptr(parent), _ptr(cu_nodes), batch, n, int(max_nodes), k,
                                 words if k == TV_MASK_BITS else 0, _ptr(o.get("bits")),
                                 _ptr(o.get("anchor_pos")), _ptr(o.get("branch_depth")),
-                                _ptr(o["depth"]), _ptr(o["err"]), _stream(stream))
+                                _ptr(o["depth"]), _ptr(o["err"]), _stream())
     _check("tv_tree_mask_build", st)
     o["kind"] = kind
     o["words_per_node"] = words if k == TV_MASK_BITS else 0
@@ -156,11 +195,29 @@ def verify_attn_workspace_size(batch: int, total_nodes: int, max_nodes: int, max
                                                       num_q_heads, num_kv_heads, head_dim, dt))
 
 
+@_on_stream
+def verify_attn_plan(batch: int, total_nodes: int, max_nodes: int, max_prefix_len: int,
+                     num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
+                     num_cus: int = 0) -> dict:
+    """Launch plan of ``tv_tree_verify_attn`` for ``num_cus`` compute units
+    (0 = the current device's): rows per block, row blocks, key splits, keys
+    per split and workspace bytes."""
+    lib = load_library()
+    dt = TV_F32 if dtype == torch.float32 else TV_BF16
+    pl = AttnPlan()
+    _check("tv_tree_verify_attn_plan",
+           lib.tv_tree_verify_attn_plan(batch, total_nodes, max_nodes, max_prefix_len,
+                                        num_q_heads, num_kv_heads, head_dim, dt, num_cus,
+                                        ctypes.byref(pl)))
+    return {f: getattr(pl, f) for f, _ in AttnPlan._fields_}
+
+
+@_on_stream
 def tree_verify_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                      block_table: torch.Tensor, prefix_len: torch.Tensor, cu_nodes: torch.Tensor,
                      mask: dict, max_nodes: int, max_prefix_len: int, scale: float | None = None,
                      out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True,
-                     workspace: torch.Tensor | None = None, stream=None):
+                     workspace: torch.Tensor | None = None):
     """One tree-verification attention layer (``tv_tree_verify_attn``).
 
     ``q`` [N, Hq, D]; ``k_cache`` [pages, Hkv, page, D], ``v_cache`` [pages, Hkv, D, page]
@@ -193,35 +250,38 @@ def tree_verify_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
                                  block_table.shape[1], _ptr(prefix_len), _ptr(cu_nodes), batch, n,
                                  int(max_nodes), int(max_prefix_len), hq, hkv, d, page, dt,
                                  float(scale), ctypes.byref(ms), _ptr(out), _ptr(lse),
-                                 _ptr(workspace), ws_bytes, _stream(stream))
+                                 _ptr(workspace), ws_bytes, _stream())
     _check("tv_tree_verify_attn", st)
     return out, lse
 
 
+@_on_stream
 def tree_accept(parent: torch.Tensor, draft_tok: torch.Tensor, target_tok: torch.Tensor,
-                cu_nodes: torch.Tensor, max_nodes: int, max_depth: int, out: dict | None = None,
-                stream=None):
+                cu_nodes: torch.Tensor, max_nodes: int, max_depth: int, out: dict | None = None):
     """Greedy acceptance (``tv_tree_accept``): returns (accept_len [B], path [B, max_depth+1], bonus [B])."""
     lib = load_library()
     dev = parent.device
     batch = cu_nodes.numel() - 1
     o = dict(out or {})
-    o.setdefault("accept_len", torch.empty(batch, dtype=torch.int32, device=dev))
-    o.setdefault("path", torch.empty((batch, max_depth + 1), dtype=torch.int32, device=dev))
-    o.setdefault("bonus", torch.empty(batch, dtype=torch.int32, device=dev))
+    if "accept_len" not in o:
+        o["accept_len"] = torch.empty(batch, dtype=torch.int32, device=dev)
+    if "path" not in o:
+        o["path"] = torch.empty((batch, max_depth + 1), dtype=torch.int32, device=dev)
+    if "bonus" not in o:
+        o["bonus"] = torch.empty(batch, dtype=torch.int32, device=dev)
     st = lib.tv_tree_accept(_ptr(parent), _ptr(draft_tok), _ptr(target_tok), _ptr(cu_nodes), batch,
                             parent.numel(), int(max_nodes), int(max_depth), _ptr(o["accept_len"]),
-                            _ptr(o["path"]), _ptr(o["bonus"]), _stream(stream))
+                            _ptr(o["path"]), _ptr(o["bonus"]), _stream())
     _check("tv_tree_accept", st)
     return o["accept_len"], o["path"], o["bonus"]
 
 
+@_on_stream
 def tree_accept_sampled(parent: torch.Tensor, draft_tok: torch.Tensor, cu_nodes: torch.Tensor,
                         target_logits: torch.Tensor, draft_logits: torch.Tensor,
                         u_accept: torch.Tensor, u_bonus: torch.Tensor, max_nodes: int,
                         max_children: int, max_depth: int, temperature: float = 1.0,
-                        workspace: torch.Tensor | None = None, out: dict | None = None,
-                        stream=None):
+                        workspace: torch.Tensor | None = None, out: dict | None = None):
     """Stochastic acceptance (``tv_tree_accept_sampled``): recursive rejection
     sampling over both models' next-token logits [N, V] (bf16 or fp32) with
     the given uniforms (fp32, ``u_accept`` [N], ``u_bonus`` [B]).
@@ -239,9 +299,12 @@ def tree_accept_sampled(parent: torch.Tensor, draft_tok: torch.Tensor, cu_nodes:
     assert u_accept.numel() == n and u_bonus.numel() == batch
     dt = TV_F32 if target_logits.dtype == torch.float32 else TV_BF16
     o = dict(out or {})
-    o.setdefault("accept_len", torch.empty(batch, dtype=torch.int32, device=dev))
-    o.setdefault("path", torch.empty((batch, max_depth + 1), dtype=torch.int32, device=dev))
-    o.setdefault("bonus", torch.empty(batch, dtype=torch.int32, device=dev))
+    if "accept_len" not in o:
+        o["accept_len"] = torch.empty(batch, dtype=torch.int32, device=dev)
+    if "path" not in o:
+        o["path"] = torch.empty((batch, max_depth + 1), dtype=torch.int32, device=dev)
+    if "bonus" not in o:
+        o["bonus"] = torch.empty(batch, dtype=torch.int32, device=dev)
     need = int(lib.tv_tree_accept_sampled_workspace_size(n, int(max_children),
                                                          target_logits.shape[1]))
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
@@ -251,7 +314,7 @@ def tree_accept_sampled(parent: torch.Tensor, draft_tok: torch.Tensor, cu_nodes:
         _ptr(parent), _ptr(draft_tok), _ptr(cu_nodes), batch, n, int(max_nodes), int(max_children),
         int(max_depth), _ptr(target_logits), _ptr(draft_logits), dt, target_logits.shape[1],
         float(temperature), _ptr(u_accept), _ptr(u_bonus), _ptr(o["accept_len"]), _ptr(o["path"]),
-        _ptr(o["bonus"]), _ptr(workspace), ws_bytes, _stream(stream))
+        _ptr(o["bonus"]), _ptr(workspace), ws_bytes, _stream())
     _check("tv_tree_accept_sampled", st)
     return o["accept_len"], o["path"], o["bonus"]
 
@@ -262,8 +325,8 @@ def tree_accept_sampled_workspace_size(total_nodes: int, max_children: int, voca
                                                                      vocab))
 
 
-def dcut_select(conf: torch.Tensor, tokens: torch.Tensor, budget: int, out: dict | None = None,
-                stream=None):
+@_on_stream
+def dcut_select(conf: torch.Tensor, tokens: torch.Tensor, budget: int, out: dict | None = None):
     """D-cut budget (``tv_dcut_select``): ``conf`` fp32 [B, D], ``tokens`` int32 [B, D+1].
 
     Returns (n_keep [B], cu_nodes [B+1], parent [budget], packed_tokens [budget]).
@@ -275,19 +338,24 @@ def dcut_select(conf: torch.Tensor, tokens: torch.Tensor, budget: int, out: dict
     assert tuple(tokens.shape) == (batch, d + 1)
     dev = conf.device
     o = dict(out or {})
-    o.setdefault("n_keep", torch.empty(batch, dtype=torch.int32, device=dev))
-    o.setdefault("cu_nodes", torch.empty(batch + 1, dtype=torch.int32, device=dev))
-    o.setdefault("parent", torch.empty(max(int(budget), 1), dtype=torch.int32, device=dev))
-    o.setdefault("packed_tokens", torch.empty(max(int(budget), 1), dtype=torch.int32, device=dev))
+    if "n_keep" not in o:
+        o["n_keep"] = torch.empty(batch, dtype=torch.int32, device=dev)
+    if "cu_nodes" not in o:
+        o["cu_nodes"] = torch.empty(batch + 1, dtype=torch.int32, device=dev)
+    if "parent" not in o:
+        o["parent"] = torch.empty(max(int(budget), 1), dtype=torch.int32, device=dev)
+    if "packed_tokens" not in o:
+        o["packed_tokens"] = torch.empty(max(int(budget), 1), dtype=torch.int32, device=dev)
     st = lib.tv_dcut_select(_ptr(conf), _ptr(tokens), batch, d, int(budget), _ptr(o["n_keep"]),
                             _ptr(o["cu_nodes"]), _ptr(o["parent"]), _ptr(o["packed_tokens"]),
-                            _stream(stream))
+                            _stream())
     _check("tv_dcut_select", st)
     return o["n_keep"], o["cu_nodes"], o["parent"][:budget], o["packed_tokens"][:budget]
 
 
+@_on_stream
 def e2e_tv_stats(target_logits: torch.Tensor, draft_logits: torch.Tensor,
-                 cu_branches: torch.Tensor | None, temperature: float = 1.0, stream=None):
+                 cu_branches: torch.Tensor | None, temperature: float = 1.0):
     """SpecOPD E2E-TV statistics (``tv_e2e_tv_stats``): logits [N, V] (bf16 or fp32).
 
     Returns (alpha [N], prefix_prob [N] or None, expected_len [B] or None), fp32.
@@ -306,13 +374,14 @@ def e2e_tv_stats(target_logits: torch.Tensor, draft_logits: torch.Tensor,
     cu = _dev_i32(cu_branches, dev) if nb else None
     st = lib.tv_e2e_tv_stats(_ptr(target_logits), _ptr(draft_logits), dt, n, v,
                              float(temperature), _ptr(cu), nb, _ptr(alpha), _ptr(prefix),
-                             _ptr(expected), _stream(stream))
+                             _ptr(expected), _stream())
     _check("tv_e2e_tv_stats", st)
     return alpha, prefix, expected
 
 
+@_on_stream
 def graft_retrieve(adj: torch.Tensor, root_tokens: torch.Tensor, tmpl_parent, tmpl_rank,
-                   out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                   out: torch.Tensor | None = None) -> torch.Tensor:
     """Graft retrieval (``tv_graft_retrieve``): ``adj`` int32 [V, k], template as host lists.
 
     Returns int32 [B, T] retrieved tokens (-1 where there is none).
@@ -327,7 +396,7 @@ def graft_retrieve(adj: torch.Tensor, root_tokens: torch.Tensor, tmpl_parent, tm
     if out is None:
         out = torch.empty((roots.numel(), len(tmpl_parent)), dtype=torch.int32, device=adj.device)
     st = lib.tv_graft_retrieve(_ptr(adj), v, k, _ptr(roots), roots.numel(), par, rank,
-                               len(tmpl_parent), _ptr(out), _stream(stream))
+                               len(tmpl_parent), _ptr(out), _stream())
     _check("tv_graft_retrieve", st)
     return out
 
@@ -338,8 +407,9 @@ def graft_update_workspace_size(num_nodes: int, vocab: int, k: int, dtype=torch.
     return int(load_library().tv_graft_update_workspace_size(num_nodes, vocab, k, dt))
 
 
+@_on_stream
 def graft_update(adj: torch.Tensor, target_logits: torch.Tensor, node_tokens: torch.Tensor,
-                 workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                 workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Graft online update (``tv_graft_update``), in place on ``adj`` int32 [V, k].
 
     ``workspace`` (uint8, device) is allocated here when absent or too small.
@@ -358,6 +428,6 @@ def graft_update(adj: torch.Tensor, target_logits: torch.Tensor, node_tokens: to
         workspace = torch.empty(need, dtype=torch.uint8, device=adj.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.tv_graft_update(_ptr(adj), v, k, _ptr(target_logits), dt, n, _ptr(tok),
-                             _ptr(workspace), ws_bytes, _stream(stream))
+                             _ptr(workspace), ws_bytes, _stream())
     _check("tv_graft_update", st)
     return adj
