@@ -9,8 +9,9 @@
  * in double precision (inputs are float32 arrays that hold exactly the values
  * the GPU receives; bf16 inputs are upcast exactly before they get here).
  * One exception: the D-cut scores decide an integer (which positions are
- * kept), so they are formed in fp32, in the same order the library forms
- * them, and the decision is taken on those values.
+ * kept), so they are formed in fp32 as [D-cut] technical summary §2 defines
+ * them -- the product of a block's confidences up to the position, taken left
+ * to right along the block -- and the decision is taken on those values.
  *
  * Sources (the four web pages on candidate-tree speculative decoding):
  *   [Graft]      Graft, arXiv:2605.20104 (163.com article "浙江大学、阿里巴巴联手破解AI推理瓶颈")
@@ -299,6 +300,14 @@ void orc_accept(const int32_t* parent, const int32_t* draft_tok,
     const int32_t* par = parent + n0;
     const int32_t* dr = draft_tok + n0;
     const int32_t* tg = target_tok + n0;
+    int32_t* prow = path + (size_t)b * (max_depth + 1);
+    for (int t = 0; t <= max_depth; ++t) prow[t] = -1;
+    if (n <= 0) {
+      /* no tree, so no root: nothing accepted, no path, no bonus token */
+      accept_len[b] = 0;
+      bonus_tok[b] = -1;
+      continue;
+    }
     int best = 0, best_depth = 0;
     for (int v = 0; v < n; ++v) {
       int ok = 1, dep = 0;
@@ -310,8 +319,6 @@ void orc_accept(const int32_t* parent, const int32_t* draft_tok,
     }
     accept_len[b] = best_depth;
     bonus_tok[b] = tg[best];
-    int32_t* prow = path + (size_t)b * (max_depth + 1);
-    for (int t = 0; t <= max_depth; ++t) prow[t] = -1;
     for (int j = best, t = best_depth; j != -1; j = par[j], --t)
       if (t <= max_depth) prow[t] = j;
   }

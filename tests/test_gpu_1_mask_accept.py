@@ -199,3 +199,29 @@ def test_accept_chains_and_repeated_siblings():
     w.target_tok[-5:] = [7, 9, 9, 0, 0]
     al = _check_accept(w)
     assert al[-1] == 2
+
+
+def test_accept_empty_requests_first_middle_last():
+    """Requests with no nodes (first, in the middle, twice in a row, last):
+    accept_len 0, path all -1, bonus -1; the others match the oracle."""
+    rng = np.random.default_rng(5)
+    trees = [W.random_tree(rng, n) for n in (7, 1, 30, 100)]
+    for layout in ([None, 0, 1], [0, None, None, 2], [3, 1, None], [None]):
+        sub = [trees[k] if k is not None else [] for k in layout]
+        par, cu = _pack(sub)
+        dr = rng.integers(4, size=len(par)).astype(np.int32)
+        tg = rng.integers(4, size=len(par)).astype(np.int32)
+        dev = "cuda"
+        if len(par) == 0:
+            par, dr, tg = np.zeros(1, np.int32), np.zeros(1, np.int32), np.zeros(1, np.int32)
+        al, path, bonus = tv.tree_accept(torch.from_numpy(par).to(dev), torch.from_numpy(dr).to(dev),
+                                         torch.from_numpy(tg).to(dev), torch.from_numpy(cu).to(dev),
+                                         128, 12)
+        oal, opath, obonus = oracle.accept(par, dr, tg, cu, 12)
+        np.testing.assert_array_equal(al.cpu().numpy(), oal)
+        np.testing.assert_array_equal(path.cpu().numpy(), opath)
+        np.testing.assert_array_equal(bonus.cpu().numpy(), obonus)
+        for b, k in enumerate(layout):
+            if k is None:
+                assert oal[b] == 0 and obonus[b] == -1 and (opath[b] == -1).all()
+

@@ -369,6 +369,34 @@ def test_appending_nodes_never_shortens_acceptance(oracle_lib, seed):
         prev = cur
 
 
+def test_empty_requests_accept_nothing_and_leave_the_others_alone(oracle_lib):
+    # A request with no nodes has no root, so nothing is accepted: length 0,
+    # an all -1 path and no bonus token (-1). Every other request of the batch
+    # gets exactly what it gets alone, whether the empty ones come first, in
+    # the middle or last (the read of the next request's nodes is the mistake
+    # this guards against).
+    rng = np.random.default_rng(11)
+    trees = [W.random_tree(rng, n) for n in (7, 1, 30)]
+    toks = [(list(rng.integers(4, size=len(t))), list(rng.integers(4, size=len(t))))
+            for t in trees]
+    alone = [oracle.accept(t, d, g, [0, len(t)], 12) for t, (d, g) in zip(trees, toks)]
+    for layout in ([None, 0, 1, 2], [0, None, None, 1, 2], [0, 1, 2, None]):
+        par, dr, tg, cu = [], [], [], [0]
+        for k in layout:
+            if k is not None:
+                par += trees[k]
+                dr += toks[k][0]
+                tg += toks[k][1]
+            cu.append(len(par))
+        al, path, bonus = oracle.accept(par, dr, tg, cu, 12)
+        for b, k in enumerate(layout):
+            if k is None:
+                assert al[b] == 0 and bonus[b] == -1 and (path[b] == -1).all(), layout
+            else:
+                assert al[b] == alone[k][0][0] and bonus[b] == alone[k][2][0], layout
+                np.testing.assert_array_equal(path[b], alone[k][1][0])
+
+
 def test_repeated_sibling_tokens_pick_deepest_then_smallest_index(oracle_lib):
     # root -> {1, 2} both carry token 7 and both match; 2 has an accepted child.
     par = [-1, 0, 0, 2, 1]
