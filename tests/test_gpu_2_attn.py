@@ -15,7 +15,7 @@ import torch
 import oracle
 import tree_verification_attention_mask_amd as tv
 import workloads as W
-from tv_testlib import Dev, assert_attn_close, oracle_attn
+from tv_testlib import Dev, all_rows, assert_attn_close, oracle_attn, oracle_attn_threaded
 
 pytestmark = pytest.mark.gpu
 
@@ -302,3 +302,55 @@ def test_empty_requests_in_batch(layout):
     d, out, lse = _run_and_check(w, "empty requests, " + layout)
     err = d.mask()["err"].cpu().numpy()
     assert err.tolist() == [0 if len(t) else 1 for t in trees]
+
+
+# ---- the 256-row blocks (two 16-row subtiles a wave), compared on whole outputs --
+# The plan takes them when a kv head has more than 128 rows and at least 48
+# key tiles (the long-context and SpecOPD workloads); these sizes reach them
+# while the oracle still recomputes every output element in seconds.
+
+def _full_output_check(w, what, mask=None, expect_rows=256):
+    pl = tv.verify_attn_plan(w.batch, w.total_nodes, w.max_nodes, w.max_prefix_len,
+                             w.num_q_heads, w.num_kv_heads, w.head_dim, torch.bfloat16)
+    assert pl["rows_per_block"] == expect_rows, pl
+    print(what, "plan", pl, flush=True)
+    d = Dev(w)
+    out, lse = d.attn(mask=mask if mask is not None else d.mask())
+    torch.cuda.synchronize()
+    ref, rlse = oracle_attn_threaded(w)
+    rows = all_rows(w)
+    got = out[rows[:, 0], rows[:, 1]].float().cpu().numpy()
+    gl = lse[rows[:, 0], rows[:, 1]].cpu().numpy()
+    st = assert_attn_close(got, ref, "bf16", gl, rlse, what=what)
+    print(what, st)
+
+
+def test_specopd_shape_256_row_blocks_whole_output():
+    """SpecOPD §02 proposal tree at a trunk of 3072 with 16 anchor branches of
+    16 (3328 nodes, 52 key tiles): ANCHOR mask, causal trunk blocks of every
+    length from 1 to 48 tiles, branch blocks skipping the tiles past their
+    anchors."""
+    w = W.make(5, trunk=3072, n_anchors=16, anchor_lo=768)
+    _full_output_check(w, "specopd trunk 3072 x 16x16")
+
+
+def test_long_context_shape_256_row_blocks_whole_output():
+    """Graft §四 long-context shape (64 query / 8 kv heads, permuted 16-token
+    pages) at one request with a 3072-key prefix (49 tiles): two 256-row
+    blocks per kv head, the second one partly padding."""
+    w = W.make(4, batch=1, prefix=3072)
+    _full_output_check(w, "long-context b1 P=3072")
+
+
+def test_wide_bits_mask_256_row_blocks_whole_output():
+    """BITS masks of more than two words (read per masked tile) in 256-row
+    blocks: trees of 200 and 130 nodes (4 and 3 words used of 4) behind
+    3000- and 2900-key prefixes (50 tiles)."""
+    rng = np.random.default_rng(256)
+    trees = [W.random_tree(rng, 200, max_children=3), W.random_tree(rng, 130, max_children=2)]
+    w = W.build_workload("wide bits", trees, [3000, 2900], 16, 4, 128, "bf16", rng,
+                         permute_pages=True, spare_pages=3, tokens=False)
+    d = Dev(w)
+    m = d.mask("bits", words=4)
+    _full_output_check(w, "wide bits 200+130 nodes", mask=m)
+

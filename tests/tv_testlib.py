@@ -45,6 +45,39 @@ class Dev:
         return tv.tree_accept(self.parent, self.draft, self.target, self.cu, self.w.max_nodes, md)
 
 
+def oracle_threads():
+    """Host threads for oracle runs: the affinity set, at most 16 (the C
+    routine runs outside the interpreter lock, one row range per thread)."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def all_rows(w, nodes=None):
+    """(node, q head) rows of the listed global nodes (default: every node)."""
+    nodes = np.arange(w.total_nodes) if nodes is None else np.asarray(nodes)
+    return np.stack(np.meshgrid(nodes, np.arange(w.num_q_heads), indexing="ij"),
+                    -1).reshape(-1, 2).astype(np.int32)
+
+
+def oracle_attn_threaded(w, rows=None):
+    """The oracle over ``rows`` (default: all rows), cut into equal row ranges
+    run on host threads; returns (out [R, D], lse [R]) in row order."""
+    from concurrent.futures import ThreadPoolExecutor
+    rows = all_rows(w) if rows is None else np.asarray(rows, np.int32)
+    q = w.q.float().numpy()
+    k = w.k_cache.float().numpy()
+    v = w.v_cache.float().numpy()
+    parts = [c for c in np.array_split(rows, oracle_threads() * 4) if len(c)]
+
+    def run(c):
+        return oracle.tree_attn(q, k, v, w.block_table, w.prefix_len, w.cu_nodes, w.parent,
+                                w.num_q_heads, w.num_kv_heads, w.scale, rows=c)
+
+    with ThreadPoolExecutor(oracle_threads()) as ex:
+        res = list(ex.map(run, parts))
+    return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])
+
+
 def oracle_attn(w, rows=None, k=None, v=None, q=None):
     return oracle.tree_attn(w.q if q is None else q, w.k_cache if k is None else k,
                             w.v_cache if v is None else v, w.block_table, w.prefix_len,
