@@ -169,6 +169,106 @@ def cpu_baseline_threads(w, seconds):
                          cpu_model(), len(os.sched_getaffinity(0)))}
 
 
+def measure_other(cfg, steps, dev):
+    """tree_verify_attn on another workload, timed like the headline's
+    attention figure: HIP-graph replays of at least 8 back-to-back calls over
+    rotating buffer sets (R sets with R x working set >= 512 MB), HIP events
+    on the launch stream, one warm replay first; plus the whole step (mask,
+    attention, acceptance) the same way. Returns the figures against the
+    roofline that bounds the workload: HBM for KV-bound shapes, MFMA for the
+    long-context and SpecOPD shapes."""
+    import torch
+
+    import tree_verification_attention_mask_amd as tv
+    import workloads as W
+    w = W.make(cfg)
+    alg_bytes, alg_flops = algorithmic_work(w)
+    set_bytes = 2 * w.k_cache.numel() * w.k_cache.element_size() + 2 * w.q.numel() * w.q.element_size()
+    R = max(1, min(64, math.ceil(512e6 / set_bytes)))
+    parent = torch.from_numpy(w.parent).to(dev)
+    cu = torch.from_numpy(w.cu_nodes).to(dev)
+    prefix = torch.from_numpy(w.prefix_len).to(dev)
+    table = torch.from_numpy(w.block_table).to(dev)
+    qs = [w.q.to(dev)]
+    ks = [w.k_cache.to(dev)]
+    vs = [w.v_cache.to(dev)]
+    w.q = w.k_cache = w.v_cache = None
+    for _ in range(R - 1):
+        qs.append(qs[0].clone())
+        ks.append(ks[0].clone())
+        vs.append(vs[0].clone())
+    outs = [torch.empty_like(qs[0]) for _ in range(R)]
+    lses = [torch.empty(qs[0].shape[:2], dtype=torch.float32, device=dev) for _ in range(R)]
+    need = tv.verify_attn_workspace_size(w.batch, w.total_nodes, w.max_nodes, w.max_prefix_len,
+                                         w.num_q_heads, w.num_kv_heads, w.head_dim, qs[0].dtype)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    m = tv.tree_mask_build(parent, cu, w.max_nodes, kind=w.mask_kind)
+    mk = {k_: v_ for k_, v_ in m.items()}
+    has_tok = w.draft_tok is not None
+    draft = torch.from_numpy(w.draft_tok).to(dev) if has_tok else None
+    target = torch.from_numpy(w.target_tok).to(dev) if has_tok else None
+    acc = {}
+    if has_tok:
+        al, path, bonus = tv.tree_accept(parent, draft, target, cu, w.max_nodes, w.max_depth)
+        acc = {"accept_len": al, "path": path, "bonus": bonus}
+
+    def attn(s_):
+        tv.tree_verify_attn(qs[s_], ks[s_], vs[s_], table, prefix, cu, mk, w.max_nodes,
+                            w.max_prefix_len, scale=w.scale, out=outs[s_], lse=lses[s_],
+                            workspace=ws)
+
+    def step(s_):
+        tv.tree_mask_build(parent, cu, w.max_nodes, kind=w.mask_kind, out=mk)
+        attn(s_)
+        if has_tok:
+            tv.tree_accept(parent, draft, target, cu, w.max_nodes, w.max_depth, out=acc)
+
+    for i in range(2 * R):
+        step(i % R)
+    torch.cuda.synchronize()
+    RG = max(R, 8)
+
+    def timed(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s_ in range(RG):
+                fn(s_ % R)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(2, steps // RG)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (reps * RG)
+
+    us = timed(attn)
+    us_step = timed(step)
+    gbs = alg_bytes / (us * 1e-6) / 1e9
+    tfl = alg_flops / (us * 1e-6) / 1e12
+    bound = "mfma" if cfg in (4, 5) else "hbm"
+    pl = tv.verify_attn_plan(w.batch, w.total_nodes, w.max_nodes, w.max_prefix_len,
+                             w.num_q_heads, w.num_kv_heads, w.head_dim, qs[0].dtype)
+    res = {"workload": w.name, "tree_nodes": w.total_nodes, "batch": w.batch,
+           "max_prefix_len": w.max_prefix_len, "rotating_buffer_sets": R,
+           "us_per_call": us, "step_us": us_step,
+           "tree_tokens_per_s": w.total_nodes / (us_step * 1e-6),
+           "algorithmic_bytes_per_launch": alg_bytes, "algorithmic_flops_per_launch": alg_flops,
+           "achieved_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+           "achieved_tflops": tfl, "mfma_frac": tfl / MFMA_BF16_PEAK_TFLOPS,
+           "bound": bound, "frac": (tfl / MFMA_BF16_PEAK_TFLOPS) if bound == "mfma"
+           else (gbs / HBM_PEAK_GBS),
+           "traffic": measured_traffic(w.name),
+           "plan": {k_: pl[k_] for k_ in ("rows_per_block", "row_blocks", "splits",
+                                          "keys_per_split")}}
+    del qs, ks, vs, outs, lses, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_model():
     """The host CPU's model name (for the CPU baseline's record)."""
     try:
@@ -190,6 +290,9 @@ def main():
     ap.add_argument("--rot", type=int, default=0, help="rotating buffer sets (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--other-configs", default="3,4,5",
+                    help="comma-separated workloads whose tree_verify_attn call (and whole step) "
+                         "is also timed and reported under 'configs' ('' = none)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="before timing, copy this many MiB device to device three times "
                          "(a plain copy of known size that hardware-counter passes use to "
@@ -304,6 +407,10 @@ def main():
     torch.cuda.synchronize()
     assert torch.equal(outs[0], eager_out), "graph replay differs from eager run"
     assert all(torch.equal(a, b) for a, b in zip(acc_out.values(), eager_acc))
+    # every graph the timed region replays has been replayed once before it
+    if g_rem is not None:
+        g_rem.replay()
+    torch.cuda.synchronize()
 
     reps_full = args.steps // RG
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -488,6 +595,16 @@ def main():
     }
     if next_rows:
         result["next_rows"] = next_rows
+    others = [int(c) for c in args.other_configs.split(",") if c.strip()]
+    others = [c for c in others if c != args.config]
+    if others:
+        del qs, ks, vs, outs, g_full, g_rem, g_attn
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        result["configs"] = []
+        for c in others:
+            log("timing tree_verify_attn on workload", W.CONFIG_NAMES[c])
+            result["configs"].append(measure_other(c, args.steps, dev))
     if not args.no_cpu_baseline:
         log("timing the CPU oracle (about %.0f s)" % args.cpu_seconds)
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
