@@ -218,6 +218,33 @@ tv_status_t tv_tree_verify_attn(const void* q, const void* k_cache, const void* 
                                 hipStream_t stream);
 
 /*
+ * tv_tree_verify_attn_noalloc -- tv_tree_verify_attn for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation, arguments and
+ * checks, minus the workspace. The split partials go to a scratch array of
+ * TV_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on
+ * until the process ends (its address is looked up on the first call on each
+ * device). The call allocates nothing.
+ *   Returns TV_ERR_WORKSPACE when the launch plan's partials
+ *   (tv_tree_verify_attn_workspace_size) exceed TV_NOALLOC_SCRATCH_BYTES, and
+ *   TV_ERR_HIP if the scratch address cannot be obtained.
+ * Every call on one device shares that device's scratch array: calls that
+ * overlap in time on one device (different streams, or graphs replayed
+ * concurrently) race and give undefined results. Nothing in the array needs
+ * to start at any value; it keeps whatever the last call left there.
+ */
+#define TV_NOALLOC_SCRATCH_BYTES (16u << 20)
+tv_status_t tv_tree_verify_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                        int32_t num_pages, const int32_t* block_table,
+                                        int32_t max_pages_per_req, const int32_t* prefix_len,
+                                        const int32_t* cu_nodes, int32_t batch,
+                                        int32_t total_nodes, int32_t max_nodes,
+                                        int32_t max_prefix_len, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                        int32_t dtype, float softmax_scale, const tv_mask_t* mask,
+                                        void* out, float* lse, hipStream_t stream);
+
+/*
  * tv_tree_accept -- greedy acceptance of the longest matching root path.
  *
  * SpecOPD §01: drafted tokens that agree with the target are accepted, the

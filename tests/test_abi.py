@@ -221,3 +221,24 @@ def test_product_path_never_touches_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower().replace("oracle-free", ""), f
+
+
+def test_noalloc_attention_refuses_plans_beyond_its_scratch_array():
+    """tv_tree_verify_attn_noalloc: 8 requests of 60 nodes behind 131,072-key
+    prefixes (64 query heads) plan three key splits whose partials (23 MiB)
+    exceed the 16 MiB scratch array: TV_ERR_WORKSPACE before anything is
+    enqueued; argument errors come first, as in tv_tree_verify_attn."""
+    lib = tv.load_library()
+    need = lib.tv_tree_verify_attn_workspace_size(8, 480, 60, 131072, 64, 8, 128, 1)
+    assert need > 16 << 20
+    m = binding.Mask(0, 1, 0x1000, None, None)
+
+    def call(q=FAKE, batch=8, total=480, maxp=131072, hq=64):
+        return lib.tv_tree_verify_attn_noalloc(q, FAKE, FAKE, 100000, FAKE, 8193, FAKE, FAKE,
+                                               batch, total, 60, maxp, hq, 8, 128, 16, 1,
+                                               ctypes.c_float(0.088), ctypes.byref(m), FAKE,
+                                               None, None)
+    assert call() == 3
+    assert call(q=None) == 1
+    assert call(hq=60) == 1             # 60 % 8 != 0
+

@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     tree_accept_sampled_workspace_size,
     tree_mask_build,
     tree_verify_attn,
+    tree_verify_attn_noalloc,
     verify_attn_plan,
     verify_attn_workspace_size,
 )

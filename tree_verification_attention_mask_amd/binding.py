@@ -28,7 +28,7 @@ MAX_ACCEPT_NODES = 8192
 
 # every symbol the header declares
 EXPORTS = ("tv_tree_mask_build", "tv_tree_verify_attn_workspace_size", "tv_tree_verify_attn_plan",
-           "tv_tree_verify_attn",
+           "tv_tree_verify_attn", "tv_tree_verify_attn_noalloc",
            "tv_tree_accept", "tv_dcut_select", "tv_e2e_tv_stats", "tv_graft_retrieve",
            "tv_graft_update_workspace_size", "tv_graft_update",
            "tv_tree_accept_sampled_workspace_size", "tv_tree_accept_sampled", "tv_status_string")
@@ -75,6 +75,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tv_tree_verify_attn.argtypes = [P, P, P, I, P, I, P, P, I, I, I, I, I, I, I, I, I,
                                         ctypes.c_float, ctypes.POINTER(Mask), P, P, P, S, P]
     lib.tv_tree_verify_attn.restype = ctypes.c_int
+    lib.tv_tree_verify_attn_noalloc.argtypes = [P, P, P, I, P, I, P, P, I, I, I, I, I, I, I, I, I,
+                                                ctypes.c_float, ctypes.POINTER(Mask), P, P, P]
+    lib.tv_tree_verify_attn_noalloc.restype = ctypes.c_int
     lib.tv_tree_accept.argtypes = [P, P, P, P, I, I, I, I, P, P, P, P]
     lib.tv_tree_accept.restype = ctypes.c_int
     lib.tv_dcut_select.argtypes = [P, P, I, I, I, P, P, P, P, P]
@@ -252,6 +255,34 @@ def tree_verify_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
                                  float(scale), ctypes.byref(ms), _ptr(out), _ptr(lse),
                                  _ptr(workspace), ws_bytes, _stream())
     _check("tv_tree_verify_attn", st)
+    return out, lse
+
+
+def tree_verify_attn_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                             block_table: torch.Tensor, prefix_len: torch.Tensor,
+                             cu_nodes: torch.Tensor, mask: dict, max_nodes: int,
+                             max_prefix_len: int, out: torch.Tensor, lse: torch.Tensor | None,
+                             scale: float | None = None, stream=None):
+    """``tv_tree_verify_attn_noalloc``: the same layer with the split partials
+    in the library's per-device scratch array. Nothing is allocated here
+    either: the caller passes ``out`` (and ``lse`` or None); ``stream`` (a
+    torch stream, default the current one) is used as given."""
+    lib = load_library()
+    n, hq, d = q.shape
+    pages, hkv, page, d2 = k_cache.shape
+    assert d2 == d and tuple(v_cache.shape) == (pages, hkv, d, page)
+    assert q.dtype == k_cache.dtype == v_cache.dtype == out.dtype and q.is_contiguous()
+    assert k_cache.is_contiguous() and v_cache.is_contiguous() and block_table.is_contiguous()
+    assert out.shape == q.shape and out.is_contiguous()
+    batch = cu_nodes.numel() - 1
+    dt = TV_F32 if q.dtype == torch.float32 else TV_BF16
+    ms = mask_struct(mask)
+    st = lib.tv_tree_verify_attn_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), pages, _ptr(block_table), block_table.shape[1],
+        _ptr(prefix_len), _ptr(cu_nodes), batch, n, int(max_nodes), int(max_prefix_len), hq, hkv,
+        d, page, dt, float(d ** -0.5 if scale is None else scale), ctypes.byref(ms), _ptr(out),
+        _ptr(lse), _stream(stream))
+    _check("tv_tree_verify_attn_noalloc", st)
     return out, lse
 
 

@@ -1,13 +1,40 @@
 // tv_api.hip -- the library's C ABI: host-side argument checks, launch plans,
 // kernel launches. Nothing here allocates, frees or synchronises.
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "tv_launch.h"
 
 using namespace tv;
 
+// Scratch memory of tv_tree_verify_attn_noalloc: the split partials live in
+// this file-scope device array instead of a caller workspace. Each device the
+// library runs on holds its own copy until the process ends. Host code never
+// uses the array's name as an address: its device address is taken once per
+// device with hipGetSymbolAddress and kept below.
+static __device__ __align__(256) unsigned char scratch[TV_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 inline tv_status_t launched(hipError_t e) { return e == hipSuccess ? TV_OK : TV_ERR_HIP; }
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch;  // per device: device address of `scratch`, or null
+
+// Device address of this device's copy of `scratch` (looked up on the first
+// call on each device, with that device current); null if HIP cannot give it.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((size_t)dev >= g_scratch.size()) g_scratch.resize(dev + 1, nullptr);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch[dev] = ptr;
+  }
+  return g_scratch[dev];
+}
 // the attention plan aims at one workgroup per compute unit of the current
 // device; MI355X's 256 when HIP cannot report the count
 inline int32_t plan_cus() {
@@ -83,13 +110,19 @@ extern "C" tv_status_t tv_tree_verify_attn_plan(int32_t batch, int32_t total_nod
   return TV_OK;
 }
 
-extern "C" tv_status_t tv_tree_verify_attn(
-    const void* q, const void* k_cache, const void* v_cache, int32_t num_pages,
-    const int32_t* block_table, int32_t max_pages_per_req, const int32_t* prefix_len,
-    const int32_t* cu_nodes, int32_t batch, int32_t total_nodes, int32_t max_nodes,
-    int32_t max_prefix_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-    int32_t page_size, int32_t dtype, float softmax_scale, const tv_mask_t* mask, void* out,
-    float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// Host-side checks of an attention call and its launch plan (shared by the
+// workspace and the scratch-array entry points). On TV_OK, `args` and `plan`
+// are filled in; the workspace itself is checked by the caller.
+tv_status_t prepare_attn(const void* q, const void* k_cache, const void* v_cache,
+                         int32_t num_pages, const int32_t* block_table, int32_t max_pages_per_req,
+                         const int32_t* prefix_len, const int32_t* cu_nodes, int32_t batch,
+                         int32_t total_nodes, int32_t max_nodes, int32_t max_prefix_len,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t page_size, int32_t dtype, float softmax_scale,
+                         const tv_mask_t* mask, void* out, float* lse, AttnArgs& a,
+                         AttnPlan& plan) {
   if (!q || !k_cache || !v_cache || !block_table || !prefix_len || !cu_nodes || !mask || !out)
     return TV_ERR_INVALID_ARGUMENT;
   if (batch < 1 || total_nodes < 1 || max_nodes < 1 || max_prefix_len < 0 || num_pages < 1 ||
@@ -114,15 +147,11 @@ extern "C" tv_status_t tv_tree_verify_attn(
   } else {
     return TV_ERR_INVALID_ARGUMENT;
   }
-  const AttnPlan plan = plan_attn(batch, total_nodes, max_nodes, max_prefix_len, num_q_heads,
-                                  num_kv_heads, head_dim, dtype, plan_cus());
+  plan = plan_attn(batch, total_nodes, max_nodes, max_prefix_len, num_q_heads, num_kv_heads,
+                   head_dim, dtype, plan_cus());
   if ((int64_t)batch * num_kv_heads * plan.row_blocks * plan.splits >= (int64_t(1) << 31))
     return TV_ERR_UNSUPPORTED;
-  if (plan.workspace > 0) {
-    if (!workspace || workspace_bytes < plan.workspace) return TV_ERR_WORKSPACE;
-    if (reinterpret_cast<uintptr_t>(workspace) & 255) return TV_ERR_INVALID_ARGUMENT;
-  }
-  AttnArgs a{};
+  a = AttnArgs{};
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
@@ -144,7 +173,55 @@ extern "C" tv_status_t tv_tree_verify_attn(
   a.mask = md;
   a.out = out;
   a.lse = lse;
+  return TV_OK;
+}
+
+}  // namespace
+
+extern "C" tv_status_t tv_tree_verify_attn(
+    const void* q, const void* k_cache, const void* v_cache, int32_t num_pages,
+    const int32_t* block_table, int32_t max_pages_per_req, const int32_t* prefix_len,
+    const int32_t* cu_nodes, int32_t batch, int32_t total_nodes, int32_t max_nodes,
+    int32_t max_prefix_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t page_size, int32_t dtype, float softmax_scale, const tv_mask_t* mask, void* out,
+    float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  AttnArgs a;
+  AttnPlan plan;
+  const tv_status_t st = prepare_attn(q, k_cache, v_cache, num_pages, block_table,
+                                      max_pages_per_req, prefix_len, cu_nodes, batch, total_nodes,
+                                      max_nodes, max_prefix_len, num_q_heads, num_kv_heads,
+                                      head_dim, page_size, dtype, softmax_scale, mask, out, lse, a,
+                                      plan);
+  if (st != TV_OK) return st;
+  if (plan.workspace > 0) {
+    if (!workspace || workspace_bytes < plan.workspace) return TV_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255) return TV_ERR_INVALID_ARGUMENT;
+  }
   a.workspace = workspace;
+  return launched(launch_attn(a, plan, stream));
+}
+
+extern "C" tv_status_t tv_tree_verify_attn_noalloc(
+    const void* q, const void* k_cache, const void* v_cache, int32_t num_pages,
+    const int32_t* block_table, int32_t max_pages_per_req, const int32_t* prefix_len,
+    const int32_t* cu_nodes, int32_t batch, int32_t total_nodes, int32_t max_nodes,
+    int32_t max_prefix_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t page_size, int32_t dtype, float softmax_scale, const tv_mask_t* mask, void* out,
+    float* lse, hipStream_t stream) {
+  AttnArgs a;
+  AttnPlan plan;
+  const tv_status_t st = prepare_attn(q, k_cache, v_cache, num_pages, block_table,
+                                      max_pages_per_req, prefix_len, cu_nodes, batch, total_nodes,
+                                      max_nodes, max_prefix_len, num_q_heads, num_kv_heads,
+                                      head_dim, page_size, dtype, softmax_scale, mask, out, lse, a,
+                                      plan);
+  if (st != TV_OK) return st;
+  if (plan.workspace > (size_t)TV_NOALLOC_SCRATCH_BYTES) return TV_ERR_WORKSPACE;
+  a.workspace = nullptr;
+  if (plan.workspace > 0) {
+    a.workspace = scratch_address();
+    if (!a.workspace) return TV_ERR_HIP;
+  }
   return launched(launch_attn(a, plan, stream));
 }
 
