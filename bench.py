@@ -201,7 +201,7 @@ def measure_other(cfg, steps, dev):
     lses = [torch.empty(qs[0].shape[:2], dtype=torch.float32, device=dev) for _ in range(R)]
     need = tv.verify_attn_workspace_size(w.batch, w.total_nodes, w.max_nodes, w.max_prefix_len,
                                          w.num_q_heads, w.num_kv_heads, w.head_dim, qs[0].dtype)
-    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
     m = tv.tree_mask_build(parent, cu, w.max_nodes, kind=w.mask_kind)
     mk = {k_: v_ for k_, v_ in m.items()}
     has_tok = w.draft_tok is not None
@@ -338,7 +338,7 @@ def main():
     lses = [torch.empty(q0.shape[:2], dtype=torch.float32, device=dev) for _ in range(R)]
     need = tv.verify_attn_workspace_size(w.batch, w.total_nodes, w.max_nodes, w.max_prefix_len,
                                          w.num_q_heads, w.num_kv_heads, w.head_dim, q0.dtype)
-    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
     mask_out = {}
     acc_out = {}
     m = tv.tree_mask_build(parent, cu, w.max_nodes, kind=w.mask_kind)

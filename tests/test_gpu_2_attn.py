@@ -354,3 +354,40 @@ def test_wide_bits_mask_256_row_blocks_whole_output():
     m = d.mask("bits", words=4)
     _full_output_check(w, "wide bits 200+130 nodes", mask=m)
 
+
+@pytest.mark.parametrize("shape", ["graft-p2048", "three-requests-hkv2", "many-splits"])
+def test_split_merge_reads_this_calls_partials(shape):
+    """Short key splits (the one-shot kernel, blocks of one group on one XCD)
+    merged by the merge kernel: every workspace byte is set to 0xFF (NaN as
+    bf16 and fp32) before each of three calls on different Q, so a merge
+    that read anything but this call's partials would give NaN or the
+    previous call's rows. Shapes: the Graft tree behind 2048 keys (16 groups,
+    11 splits), three requests over 2 kv heads (groups not a multiple of 8),
+    one request split 17 ways."""
+    rng = np.random.default_rng(len(shape))
+    if shape == "graft-p2048":
+        w = W.make(2)
+    elif shape == "three-requests-hkv2":
+        trees = [list(W.GRAFT_TREE_PARENT), W.random_tree(rng, 40), W.random_tree(rng, 7)]
+        w = W.build_workload("merge3", trees, [900, 1200, 700], 8, 2, 128, "bf16", rng,
+                             permute_pages=True, spare_pages=2, tokens=False)
+    else:
+        w = W.build_workload("merge17", [W.random_tree(rng, 20)], [2100], 8, 8, 64, "bf16", rng,
+                             tokens=False)
+    pl = tv.verify_attn_plan(w.batch, w.total_nodes, w.max_nodes, w.max_prefix_len,
+                             w.num_q_heads, w.num_kv_heads, w.head_dim, torch.bfloat16)
+    print(shape, pl, flush=True)
+    assert pl["splits"] > 1 and pl["keys_per_split"] <= 256 and pl["rows_per_block"] == 128
+    d = Dev(w)
+    m = d.mask()
+    ws = torch.empty(pl["workspace_bytes"], dtype=torch.uint8, device="cuda")
+    q0 = w.q.clone()
+    for call in range(3):
+        w.q = (q0 * (1.0 + 0.5 * call)).to(q0.dtype)
+        d.q = w.q.cuda()
+        ws.fill_(255)
+        out, lse = d.attn(mask=m, workspace=ws)
+        torch.cuda.synchronize()
+        ref, rlse = oracle_attn(w)
+        print(shape, call, assert_attn_close(out, ref, "bf16", lse, rlse,
+                                              what="%s call %d" % (shape, call)))

@@ -149,7 +149,7 @@ tv_status_t prepare_attn(const void* q, const void* k_cache, const void* v_cache
   }
   plan = plan_attn(batch, total_nodes, max_nodes, max_prefix_len, num_q_heads, num_kv_heads,
                    head_dim, dtype, plan_cus());
-  if ((int64_t)batch * num_kv_heads * plan.row_blocks * plan.splits >= (int64_t(1) << 31))
+  if (((int64_t)batch * num_kv_heads * plan.row_blocks + 7) * plan.splits >= (int64_t(1) << 31))
     return TV_ERR_UNSUPPORTED;
   a = AttnArgs{};
   a.q = q;

@@ -801,6 +801,350 @@ void attn_bf16_kernel(Params p) {
   }
 }
 
+// ---- short splits: every tile of the split in LDS at once ("one-shot").
+// When a split holds at most kShortTiles key tiles (short prefixes cut over
+// many workgroups, e.g. a 60-node tree behind a 2048-key prefix), the tile
+// loop's per-tile barriers and pipeline fill cost more than its arithmetic.
+// Here a workgroup of 8 waves (16 rows each, 128 rows) requests Q and all of
+// its tiles in one round trip. Waves w and w + 4 share a SIMD; the first four
+// (group A) compute S = K Q^T tile by tile as the tiles land, then the
+// softmax, while group B computes its S; group A's O += V^T P^T then runs
+// beside group B's softmax, so each SIMD's matrix and vector pipes overlap.
+// One softmax per row over the whole split (a single max, no rescaling).
+//
+// Blocks are numbered split-major over groups padded to a multiple of 8, so
+// every split of one (request, kv head, row block) -- and, when batch * Hkv
+// is a multiple of 8, every row block of one kv head -- is dispatched to the
+// same XCD (workgroups go round-robin over the 8 XCDs): the group's Q and
+// K/V tiles are fetched from HBM once and then hit that XCD's L2.
+//
+// With key splits, every split stores its partial (its own softmax
+// average in bf16, m and l) and the merge kernel combines them, as for the
+// tile loop. (Merging inside this kernel -- by the last split to arrive, or
+// by merge workgroups at the end of the grid -- was measured slower on this
+// GPU: the acknowledged partial stores and the arrival atomics cost more
+// than the kernel boundary they save.)
+constexpr int kShortTiles = 4;
+
+template <int D, bool WIDE>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_bf16_short_kernel(Params p) {
+  constexpr int NW = 8;
+  constexpr int T = 64 * NW;
+  constexpr int DS = D / 32;           // 32-wide d steps of S^T = K Q^T
+  constexpr int DU = D / 16;           // 16-wide d subtiles of O^T
+  constexpr int MBLK = 16 * NW;        // rows per workgroup
+  constexpr int CPR = D / 8;           // 16-byte chunks per K row
+  constexpr int TILE_E = kTile * D;
+  constexpr int K_INS = D / 8;         // 1 KB direct-to-LDS loads per K tile
+  constexpr int INS = 2 * K_INS;
+  constexpr int IPW = INS / NW;        // loads per wave per tile
+  constexpr int RPI = 512 / D;         // K rows per load
+  constexpr int VPG = D / 32;          // V loads per 16-key group
+  static_assert(IPW * RPI == 16 && IPW == VPG, "one 16-key group per wave and tile");
+  __shared__ __attribute__((aligned(16))) __bf16 sK[kShortTiles][TILE_E];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[kShortTiles][TILE_E];
+
+  const int ng = p.batch * p.hkv * p.row_blocks;
+  const int ng_pad = (ng + 7) & ~7;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int gi = blockIdx.x % ng_pad;
+  const int split = blockIdx.x / ng_pad;
+  if (gi >= ng) return;
+  const int g = gi % p.hkv;
+  const int b = (gi / p.hkv) % p.batch;
+  const int rb = gi / (p.hkv * p.batch);
+  const int ks = split * p.keys_per_split;
+
+  // this wave's 16-key group of every tile and its page id: table reads that
+  // do not wait for the request's bounds (entries past the request's pages
+  // are clamped into the pool; their keys are masked and their V zeroed)
+  const int lp = __builtin_ctz(p.page_size);
+  const int pmask = p.page_size - 1;
+  const bool k_wave = wave < NW / 2;
+  const int gw = k_wave ? wave : wave - NW / 2;
+  const int32_t* row_tab = p.block_table + (size_t)b * p.max_pages;
+  int pg[kShortTiles];
+#pragma unroll
+  for (int t = 0; t < kShortTiles; ++t)
+    pg[t] = row_tab[min((ks + kTile * t + 16 * gw) >> lp, p.max_pages - 1)];
+
+  const int n0 = clampi(p.cu_nodes[b], 0, p.total_nodes);
+  const int n = clampi(p.cu_nodes[b + 1], n0, p.total_nodes) - n0;
+  const int P = max(p.prefix_len[b], 0);
+  const int G = p.group;
+  const int rows = n * G;
+  const int row0 = rb * MBLK;
+  if (row0 >= rows) return;
+  const int kv_end = P + n;
+  // Keys [ks, ke): none when the split starts past the request's keys or
+  // past what the block's last node can see (the split then contributes
+  // an empty partial, m = -inf, l = 0).
+  const int node_hi = min(n - 1, (row0 + MBLK - 1) / G);
+  const int ke = min(min(ks + p.keys_per_split, kv_end), P + node_hi + 1);
+  const int nt = ke > ks ? (ke - ks + kTile - 1) / kTile : 0;  // tiles in range, 0 .. kShortTiles
+
+  // ---- Q fragments and mask rows (padding rows read the request's first
+  // row), requested before the tiles so they land first
+  const int row = row0 + 16 * wave + r16;
+  const bool row_ok = row < rows;
+  const bool has_rows = row0 + 16 * wave < rows;  // wave-uniform
+  const int li = row_ok ? row / G : 0;
+  const int rnode = n0 + li;
+  const int orow = rnode * p.hq + g * G + (row_ok ? row % G : 0);
+  const bool anchor = p.mask.kind == TV_MASK_ANCHOR;
+  uint64_t m_w0 = 0ull, m_w1 = 0ull;
+  if (anchor) {
+    m_w0 = (uint64_t)(uint32_t)p.mask.anchor_pos[rnode] |
+           ((uint64_t)(uint32_t)p.mask.branch_depth[rnode] << 32);
+  } else if (!WIDE) {
+    m_w0 = p.mask.bits[(size_t)rnode * p.mask.words];
+    m_w1 = p.mask.bits[(size_t)rnode * p.mask.words + (p.mask.words - 1)];
+  }
+  bf16x8 qf[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s)
+    qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                           p.q + (size_t)orow * D + 32 * s + 8 * q4));
+
+  // ---- all tiles of the split, straight into LDS (layouts as in the tile loop)
+  int lane_off[IPW], lds_off[IPW];
+#pragma unroll
+  for (int m = 0; m < IPW; ++m) {
+    const int ins = wave * IPW + m;
+    if (k_wave) {
+      const int row_k = ins * RPI + lane / CPR;
+      lane_off[m] = (lane / CPR) * D + 8 * ((lane % CPR) ^ (row_k % CPR));
+      lds_off[m] = ins * RPI * D;
+    } else {
+      const int vi = ins - K_INS, jj = vi / VPG, dp = vi % VPG;
+      lane_off[m] = ((32 * dp + lane / 2) << lp) + 8 * (lane % 2);
+      lds_off[m] = jj * 16 * D + 32 * dp * 16;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kShortTiles; ++t) {
+    if (t >= nt) break;
+    const int k0 = ks + kTile * t;
+    const long blk = (long)clampi(pg[t], 0, p.num_pages - 1) * p.hkv + g;
+    if (k_wave) {
+#pragma unroll
+      for (int m = 0; m < IPW; ++m) {
+        const int slot0 = (k0 + 16 * gw + m * RPI) & pmask;
+        lds_dma16(p.k + (((blk << lp) + slot0) * D + lane_off[m]), &sK[t][lds_off[m]]);
+      }
+    } else {
+      const int slot0 = (k0 + 16 * gw) & pmask;
+#pragma unroll
+      for (int m = 0; m < IPW; ++m)
+        lds_dma16(p.v + (((blk * D) << lp) + slot0 + lane_off[m]), &sV[t][lds_off[m]]);
+    }
+  }
+  // Q and mask rows are used from registers from here on
+#pragma unroll
+  for (int s = 0; s < DS; ++s) asm volatile("" : "+v"(qf[s]));
+  asm volatile("" : "+v"(m_w0), "+v"(m_w1));
+
+  // visibility of keys [k0, k0 + 64) for this lane's row (as in the tile loop)
+  auto row_visibility = [&](int k0) -> uint64_t {
+    if (!row_ok) return 0ull;
+    uint64_t v = range_bits(0, P - 1 - k0);
+    if (k0 + kTile > P && k0 < kv_end) {
+      const int j0 = k0 - P;
+      uint64_t t;
+      if (anchor) {
+        const int ap = (int)(uint32_t)m_w0, bd = (int)(uint32_t)(m_w0 >> 32);
+        t = range_bits(-j0, ap - j0) | range_bits(li - bd + 1 - j0, li - j0);
+      } else if (!WIDE) {
+        if (j0 < 0) {
+          t = m_w0 << (-j0);
+        } else {
+          const int sh = j0 & 63;
+          const uint64_t lo = (j0 < 64) ? m_w0 : m_w1;
+          const uint64_t hi = (j0 < 64) ? m_w1 : 0ull;
+          t = sh ? ((lo >> sh) | (hi << (64 - sh))) : lo;
+        }
+      } else {
+        return tile_visibility(p.mask, rnode, li, P, kv_end, k0);
+      }
+      v |= t & range_bits(P - k0, kv_end - 1 - k0);
+    }
+    return v;
+  };
+  // ---- S^T = K Q^T of tile t (score rows permuted as in the tile loop: the
+  // lane of row r16, column group q4 holds keys 32kk + 8q4 .. +7)
+  auto key_of = [](int t, int m) { return 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3); };
+  f32x4 sc[kShortTiles][4];
+#pragma unroll
+  for (int t = 0; t < kShortTiles; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto qk = [&](int t) {
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int krow = key_of(u, r16);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
+            &sK[t][krow * D + 8 * ((4 * s + q4) ^ (krow % CPR))]);
+        sc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sc[t][u], 0, 0, 0);
+      }
+    }
+  };
+  float m_row = -INFINITY, l_row = 0.f;
+  bf16x8 pf[kShortTiles][2];
+  // ---- mask, one row max, probabilities (bf16 B operand of PV), fp32 sums
+  auto softmax = [&]() {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kShortTiles; ++t) {
+      const int k0 = ks + kTile * t;
+      const bool live = t < nt;
+      if (live && k0 + kTile > P) {
+        const uint64_t sh = row_visibility(k0) >> (8 * q4);
+        const uint32_t own = (uint32_t)(sh & 0xffu) | ((uint32_t)(sh >> 32) & 0xffu) << 8;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sc[t][u][i] = ((own >> (4 * u + i)) & 1u) ? sc[t][u][i] : -INFINITY;
+      }
+      if (live) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[t][u][i]);
+      }
+    }
+    m_row = row_max4(mx) * p.scale_log2;  // log2 units; -inf: no visible key here
+    const float m_use = (m_row == -INFINITY) ? 0.f : m_row;
+    float l_lane = 0.f;
+#pragma unroll
+    for (int t = 0; t < kShortTiles; ++t) {
+      float part[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sc[t][u][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][u][i], p.scale_log2, -m_use));
+        part[u] = (sc[t][u][0] + sc[t][u][1]) + (sc[t][u][2] + sc[t][u][3]);
+      }
+      if (t < nt) l_lane += (part[0] + part[1]) + (part[2] + part[3]);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[i] = static_cast<__bf16>(sc[t][2 * kk][i]);
+          f[4 + i] = static_cast<__bf16>(sc[t][2 * kk + 1][i]);
+        }
+        pf[t][kk] = f;
+      }
+    }
+    l_row = row_sum4(l_lane);
+  };
+  // ---- O^T += V^T P^T
+  f32x4 o[DU];
+#pragma unroll
+  for (int u = 0; u < DU; ++u) o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto pv = [&]() {
+#pragma unroll
+    for (int t = 0; t < kShortTiles; ++t) {
+      if (t >= nt) continue;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int u = 0; u < DU; ++u) {
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
+              &sV[t][(2 * kk + (q4 >> 1)) * 16 * D + (16 * u + r16) * 16 + 8 * (q4 & 1)]);
+          o[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[t][kk], o[u], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // ---- tiles land in order: wait for this wave's loads of tile t (counted
+  // vmcnt), then the barrier publishes every wave's part of it
+  const bool grp_b = wave >= NW / 2;
+  const bool tail = nt > 0 && ks + kTile * nt > kv_end;
+#pragma unroll
+  for (int t = 0; t < kShortTiles; ++t) {
+    if (t >= nt) break;
+    const int later = nt - 1 - t;  // tiles requested after this one
+    if (later >= 3) wait_vmem<3 * IPW>();
+    else if (later == 2) wait_vmem<2 * IPW>();
+    else if (later == 1) wait_vmem<IPW>();
+    else wait_vmem<0>();
+    __builtin_amdgcn_s_barrier();
+    if (t == nt - 1 && tail) {
+      // V of the positions past the request's last key (cache slots the
+      // caller never wrote) must be finite zeros: P = 0 there. Published by
+      // the barrier below, before any PV.
+      const int lim = kv_end - (ks + kTile * t);
+      for (int c = tid; c < TILE_E / 8; c += T) {
+        const int e = 8 * c;
+        const int key0 = 16 * (e / (16 * D)) + (e & 15);
+        if (key0 + 7 < lim) continue;
+        bf16x8* ch = reinterpret_cast<bf16x8*>(&sV[t][e]);
+        bf16x8 v = *ch;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (key0 + i >= lim) ? static_cast<__bf16>(0.f) : v[i];
+        *ch = v;
+      }
+      __builtin_amdgcn_s_waitcnt(W_ALL & ~0x0F00);
+    }
+    if (!grp_b && has_rows) qk(t);
+  }
+  if (nt == 0) wait_vmem<0>();  // Q and mask rows
+  __builtin_amdgcn_s_barrier();
+  if (has_rows) {
+    if (grp_b) {
+#pragma unroll
+      for (int t = 0; t < kShortTiles; ++t)
+        if (t < nt) qk(t);
+    } else {
+      softmax();
+    }
+  }
+  __builtin_amdgcn_s_barrier();
+  if (has_rows) {
+    if (grp_b) softmax();
+    pv();
+  }
+
+  // ---- epilogue: lane (r16, q4) holds O[row r16][16u + 4q4 + i]
+  const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+  if (p.splits == 1) {
+    if (!row_ok) return;
+#pragma unroll
+    for (int u = 0; u < DU; ++u) {
+      bf16x4 h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[i] = static_cast<__bf16>(o[u][i] * inv);
+      *reinterpret_cast<bf16x4*>(p.out + (size_t)orow * D + 16 * u + 4 * q4) = h;
+    }
+    if (p.lse && q4 == 0)
+      p.lse[orow] = l_row > 0.f ? (m_row + log2f(l_row)) * kLn2 : -INFINITY;
+    return;
+  }
+  // partials for the merge kernel, [split][total_nodes * hq] rows
+  if (!row_ok) return;
+  const size_t prow = (size_t)split * p.total_nodes * p.hq + orow;
+#pragma unroll
+  for (int u = 0; u < DU; ++u) {
+    bf16x4 h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = static_cast<__bf16>(o[u][i] * inv);
+    __builtin_nontemporal_store(h, reinterpret_cast<bf16x4*>(p.part_o + prow * D + 16 * u + 4 * q4));
+  }
+  if (q4 == 0) {
+    __builtin_nontemporal_store(m_row, p.part_ml + prow * 2);
+    __builtin_nontemporal_store(l_row, p.part_ml + prow * 2 + 1);
+  }
+}
+
 // Merge of split partials: m = max m_s, l = sum 2^(m_s - m) l_s,
 // o = sum 2^(m_s - m) l_s o_s / l (o_s the split's own average, bf16),
 // lse = (m + log2 l) ln 2. One row per D/4
@@ -972,6 +1316,13 @@ hipError_t run_bf16(const Params& prm, int grid, hipStream_t stream) {
 
 template <int D>
 hipError_t dispatch_bf16(const Params& prm, const AttnPlan& plan, int grid, hipStream_t stream) {
+  if (plan.short_splits) {
+    if (prm.mask.kind == TV_MASK_BITS && prm.mask.words > 2)
+      hipLaunchKernelGGL((attn_bf16_short_kernel<D, true>), dim3(grid), dim3(512), 0, stream, prm);
+    else
+      hipLaunchKernelGGL((attn_bf16_short_kernel<D, false>), dim3(grid), dim3(512), 0, stream, prm);
+    return hipGetLastError();
+  }
   if (plan.rw == 1) return run_bf16<D, 8, 1>(prm, grid, stream);
   return run_bf16<D, 8, 2>(prm, grid, stream);
 }
@@ -1013,12 +1364,17 @@ AttnPlan plan_attn(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_
   const long tps = (tiles + splits - 1) / splits;
   pl.keys_per_split = (int)(tps * kTile);
   pl.splits = (int)((tiles + tps - 1) / tps);
+  // splits of a few tiles take the one-shot kernel (128-row blocks), which
+  // also merges them itself when there are not too many
+  pl.short_splits = (pl.rw == 1 && tps <= kShortTiles) ? 1 : 0;
   if (pl.splits > 1) {
     const size_t rtot = (size_t)total_nodes * hq;
     const size_t o_bytes = (size_t)pl.splits * rtot * head_dim * sizeof(__bf16);
     const size_t ml_bytes = (size_t)pl.splits * rtot * 2 * sizeof(float);
-    pl.workspace = ((o_bytes + 255) & ~(size_t)255) + ((ml_bytes + 255) & ~(size_t)255);
+    pl.part_ml_offset = (o_bytes + 255) & ~(size_t)255;
+    pl.workspace = pl.part_ml_offset + ((ml_bytes + 255) & ~(size_t)255);
   } else {
+    pl.part_ml_offset = 0;
     pl.workspace = 0;
   }
   return pl;
@@ -1065,9 +1421,8 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t stre
   p.lse = a.lse;
   const size_t rtot = (size_t)a.total_nodes * a.hq;
   char* ws = static_cast<char*>(a.workspace);
-  p.part_o = reinterpret_cast<__bf16*>(ws);
-  const size_t o_bytes = ((size_t)plan.splits * rtot * a.head_dim * sizeof(__bf16) + 255) & ~(size_t)255;
-  p.part_ml = plan.splits > 1 ? reinterpret_cast<float*>(ws + o_bytes) : nullptr;
+  p.part_o = plan.splits > 1 ? reinterpret_cast<__bf16*>(ws) : nullptr;
+  p.part_ml = plan.splits > 1 ? reinterpret_cast<float*>(ws + plan.part_ml_offset) : nullptr;
   p.num_pages = a.num_pages;
   p.max_pages = a.max_pages;
   p.batch = a.batch;
@@ -1080,8 +1435,9 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t stre
   p.splits = plan.splits;
   p.keys_per_split = plan.keys_per_split;
   p.scale_log2 = a.scale * kLog2e;
-  const int grid = a.batch * a.hkv * plan.row_blocks * plan.splits;
-  p.lpt = (a.batch >= 2 && a.batch <= kMaxLptBatch && grid > plan.num_cus) ? 1 : 0;
+  const int ng = a.batch * a.hkv * plan.row_blocks;
+  const int grid = plan.short_splits ? ((ng + 7) & ~7) * plan.splits : ng * plan.splits;
+  p.lpt = (!plan.short_splits && a.batch >= 2 && a.batch <= kMaxLptBatch && grid > plan.num_cus) ? 1 : 0;
   hipError_t e = (a.head_dim == 64) ? dispatch_bf16<64>(p, plan, grid, stream)
                                     : dispatch_bf16<128>(p, plan, grid, stream);
   if (e != hipSuccess || plan.splits == 1) return e;

@@ -87,6 +87,8 @@ struct AttnPlan {
   int row_blocks;      // blocks over the node*group rows of one kv head
   int splits;          // key splits
   int keys_per_split;  // multiple of 64
+  int short_splits;    // 1: splits of at most a few tiles, one-shot kernel
+  size_t part_ml_offset;  // byte offset of the (m, l) partials (o partials at 0)
   size_t workspace;    // bytes of split partials (0 when splits == 1)
 };
 // num_cus: compute units of the device the call runs on (the split count
