@@ -135,6 +135,20 @@ __device__ __forceinline__ void lds_dma16(const void* src, const void* lds) {
       : "memory");
 }
 
+// XOR swizzle of the 16-byte chunks of K row `row` in LDS: chunk c of the
+// row is stored at position c ^ kswz(row). The S^T = K Q^T fragments read
+// rows 32(t/2) + 8(r/4) + 4(t%2) + r%4 for the 16 lanes r of a column group,
+// so the swizzle must take 16 different values on row bits {0, 1, 3, 4}
+// (D = 128: 16 chunks per 256-byte row, every row on the same banks); the
+// plain row % 16 takes only 8 there and makes those reads two-way bank
+// conflicts (measured on gfx950: 127 against 215 bytes per clock for a
+// conflict-free ds_read_b128 stream).
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  if constexpr (D == 128) return (row & 3) | ((row >> 1) & 12);
+  else return row % (D / 8);
+}
+
 template <int D, int NW, int RW, bool WIDE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bf16_kernel(Params p) {
@@ -405,7 +419,7 @@ void attn_bf16_kernel(Params p) {
   // ---- direct-to-LDS staging (lds_dma16). Load m of wave w is number
   // ins = w*IPW + m of the tile: ins < K_INS copies K rows [ins*RPI, +RPI)
   // (lane l: row ins*RPI + l/CPR, whose LDS chunk l%CPR receives K chunk
-  // (l%CPR) ^ (row%CPR)); otherwise V 16-key group j = (ins-K_INS)/VPG,
+  // (l%CPR) ^ kswz(row)); otherwise V 16-key group j = (ins-K_INS)/VPG,
   // d rows 32*((ins-K_INS)%VPG) + l/2, keys 8*(l%2) .. +7. The first NW/2
   // waves load K, the others V; either way the loads of one wave cover
   // GPW whole 16-key groups, gw .. gw+GPW-1, and pages hold a power of two
@@ -420,7 +434,7 @@ void attn_bf16_kernel(Params p) {
     const int ins = wave * IPW + m;
     if (k_wave) {
       const int row = ins * RPI + lane / CPR;
-      lane_off[m] = (lane / CPR) * D + 8 * ((lane % CPR) ^ (row % CPR));
+      lane_off[m] = (lane / CPR) * D + 8 * ((lane % CPR) ^ kswz<D>(row));
       lds_off[m] = ins * RPI * D;
     } else {
       const int vi = ins - K_INS, jj = vi / VPG, dp = vi % VPG;
@@ -492,7 +506,7 @@ void attn_bf16_kernel(Params p) {
       for (int t = 0; t < 4; ++t) {
         const int krow = key_of(t, r16);
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-            &sK[buf][krow * D + 8 * ((4 * s + q4) ^ (krow % CPR))]);
+            &sK[buf][krow * D + 8 * ((4 * s + q4) ^ kswz<D>(krow))]);
 #pragma unroll
         for (int r = 0; r < RW; ++r)
           sacc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[r][s], sacc[r][t], 0, 0, 0);
@@ -916,7 +930,7 @@ void attn_bf16_short_kernel(Params p) {
     const int ins = wave * IPW + m;
     if (k_wave) {
       const int row_k = ins * RPI + lane / CPR;
-      lane_off[m] = (lane / CPR) * D + 8 * ((lane % CPR) ^ (row_k % CPR));
+      lane_off[m] = (lane / CPR) * D + 8 * ((lane % CPR) ^ kswz<D>(row_k));
       lds_off[m] = ins * RPI * D;
     } else {
       const int vi = ins - K_INS, jj = vi / VPG, dp = vi % VPG;
@@ -988,7 +1002,7 @@ void attn_bf16_short_kernel(Params p) {
       for (int u = 0; u < 4; ++u) {
         const int krow = key_of(u, r16);
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-            &sK[t][krow * D + 8 * ((4 * s + q4) ^ (krow % CPR))]);
+            &sK[t][krow * D + 8 * ((4 * s + q4) ^ kswz<D>(krow))]);
         sc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sc[t][u], 0, 0, 0);
       }
     }
