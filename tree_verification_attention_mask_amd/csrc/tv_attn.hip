@@ -296,19 +296,14 @@ void attn_bf16_kernel(Params p) {
   // treat tiles every row sees in full as unmasked.
   int ap_min = -1, ap_max = 0x7fffffff, br_lo = 0x7fffffff;
   const bool anchor = p.mask.kind == TV_MASK_ANCHOR;
-  if (anchor) {
-    if (tid == 0) { s_bounds[0] = 0x7fffffff; s_bounds[1] = -1; s_bounds[2] = 0x7fffffff; }
-    __syncthreads();
-    const int node_lo = row0 / G;
-    for (int i = node_lo + tid; i <= node_hi; i += T) {
-      const int a = p.mask.anchor_pos[n0 + i], d = p.mask.branch_depth[n0 + i];
-      atomicMin(&s_bounds[0], a);
-      atomicMax(&s_bounds[1], a);
-      if (d > 0) atomicMin(&s_bounds[2], i - d + 1);
-    }
-    __syncthreads();
-    ap_min = s_bounds[0]; ap_max = s_bounds[1]; br_lo = s_bounds[2];
-  }
+  if (anchor && tid == 0) { s_bounds[0] = 0x7fffffff; s_bounds[1] = -1; s_bounds[2] = 0x7fffffff; }
+  // V of stage STAGES-1 is read (times P = 0) by the first M cluster
+  for (int c = tid; c < TILE_E / 8; c += T)
+    reinterpret_cast<uint4*>(&sV[STAGES - 1][0])[c] = uint4{0u, 0u, 0u, 0u};
+  // the page list, the bounds' initial values and the zeros are written;
+  // make them visible
+  __builtin_amdgcn_s_waitcnt(W_ALL & ~0x0F00);
+  __syncthreads();
   // Tile [k0, k0+64): skipped when it holds no prefix key and no tree key any
   // row of the block can see; unmasked when all its keys are visible to all.
   auto skip_tile = [&](int k0) -> bool {
@@ -675,17 +670,42 @@ void attn_bf16_kernel(Params p) {
     probs(sc, pf);
   };
 
+  // The split's first two tiles are requested before the block's anchor
+  // bounds are known, while those loads and the Q and mask-row loads are in
+  // flight (one dependent round trip fewer; under load each costs a few us).
+  // Only the anchor form skips tiles, and its first tile ks is skipped only
+  // in a split that starts in the tree part past every anchor: then the
+  // tiles are requested again once the bounds are known.
+  const int spec0 = ks < ke ? ks : ke;
+  const int spec1 = spec0 + kTile < ke ? spec0 + kTile : ke;
+  int pgn[GPW];
+  if (spec0 < ke) { pages_for(spec0, pgn); issue(0, spec0, pgn); }
+  if (spec1 < ke) { pages_for(spec1, pgn); issue(1, spec1, pgn); }
+  if (anchor) {
+    // ANCHOR form: block-wide bounds to skip tree tiles no row can see and
+    // to treat tiles every row sees in full as unmasked
+    const int node_lo = row0 / G;
+    for (int i = node_lo + tid; i <= node_hi; i += T) {
+      const int a = p.mask.anchor_pos[n0 + i], d = p.mask.branch_depth[n0 + i];
+      atomicMin(&s_bounds[0], a);
+      atomicMax(&s_bounds[1], a);
+      if (d > 0) atomicMin(&s_bounds[2], i - d + 1);
+    }
+    __syncthreads();
+    ap_min = s_bounds[0]; ap_max = s_bounds[1]; br_lo = s_bounds[2];
+  }
   int c_cur = ks;
   while (c_cur < ke && skip_tile(c_cur)) c_cur += kTile;
   int c_prev = ke;  // tile m-1 (none yet)
   int c_n1 = next_tile(c_cur), c_n2 = next_tile(c_n1);
-  // V of stage STAGES-1 is read (times P = 0) by the first M cluster
-  for (int c = tid; c < TILE_E / 8; c += T)
-    reinterpret_cast<uint4*>(&sV[STAGES - 1][0])[c] = uint4{0u, 0u, 0u, 0u};
-  // the page list and the zeros are written; make them visible (Q and mask
-  // loads stay in flight)
-  __builtin_amdgcn_s_waitcnt(W_ALL & ~0x0F00);
-  barrier();
+  if (min(c_cur, ke) != spec0 || min(c_n1, ke) != spec1) {
+    // the bounds skip a requested tile: let the requests land, then ask for
+    // the right ones (a workgroup-uniform branch)
+    wait_vmem<0>();
+    barrier();
+    if (c_cur < ke) { pages_for(c_cur, pgn); issue(0, c_cur, pgn); }
+    if (c_n1 < ke) { pages_for(c_n1, pgn); issue(1, c_n1, pgn); }
+  }
   // Solo blocks: the waves of group B hold no rows (at most 16*NW/2 rows),
   // so only group A reads the tiles and the stage of tile m-1 is free once
   // slot 2m ends. Tiles are then requested three ahead, in slot 2m+1, into
@@ -693,11 +713,8 @@ void attn_bf16_kernel(Params p) {
   // HBM latency, not by the matrix cores).
   const bool solo = rows - row0 <= 16 * (NW / 2);
   int c_n3 = solo ? next_tile(c_n2) : ke;  // tile to request in slot 2m+1 (solo)
-  int pgn[GPW];
-  if (c_cur < ke) { pages_for(c_cur, pgn); issue(0, c_cur, pgn); }
-  if (c_n1 < ke) { pages_for(c_n1, pgn); issue(1, c_n1, pgn); }
   // Q fragments and mask rows are used from registers from here on (this
-  // waits for them, and for the tiles just requested)
+  // waits for them, and for the tiles requested above)
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     asm volatile("" : "+v"(m_w0[r]), "+v"(m_w1[r]));
@@ -719,6 +736,10 @@ void attn_bf16_kernel(Params p) {
       wait_vm(solo ? (c_n2 < ke ? 2 * IPW : (c_n1 < ke ? IPW : 0)) : (c_n1 < ke ? IPW : 0));
     barrier();
     if (c_cur < ke) zero_tail(m & (STAGES - 1), c_cur);
+  };
+  // tile m+2 into the stage tile m-2 left (free since the barrier that
+  // opened this step)
+  auto request = [&]() {
     if (!solo) {
       if (c_n2 < ke) issue((m + 2) & (STAGES - 1), c_n2, pgn);
       c_nn = next_tile(c_n2);
@@ -748,15 +769,18 @@ void attn_bf16_kernel(Params p) {
       cluster_m(m);
       barrier();
       mid();
+      request();
       cluster_v(c_cur);
       advance();
     }
     head();
+    request();
     cluster_m(m);  // PV of the last tile
     barrier();
   } else {
     if (c_cur < ke) {
       head();
+      request();
       barrier();
       mid();
       cluster_m(m);
@@ -764,6 +788,7 @@ void attn_bf16_kernel(Params p) {
     }
     while (c_cur < ke) {
       head();
+      request();
       cluster_v(c_prev);
       barrier();
       mid();
@@ -771,6 +796,7 @@ void attn_bf16_kernel(Params p) {
       advance();
     }
     head();
+    request();
     if (c_prev < ke) cluster_v(c_prev);
     barrier();
     cluster_m(m);  // PV of the last tile
