@@ -1169,9 +1169,12 @@ void attn_bf16_short_kernel(Params p) {
       p.lse[orow] = l_row > 0.f ? (m_row + log2f(l_row)) * kLn2 : -INFINITY;
     return;
   }
-  // partials for the merge kernel, [split][total_nodes * hq] rows
+  // partials for the merge kernel, [split][total_nodes * hq] rows; a split
+  // with no key for this block stores only its empty marker (m = -inf,
+  // l = 0: the merge never reads that split's o)
   if (!row_ok) return;
   const size_t prow = (size_t)split * p.total_nodes * p.hq + orow;
+  if (nt > 0)
 #pragma unroll
   for (int u = 0; u < DU; ++u) {
     bf16x4 h;
