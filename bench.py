@@ -560,6 +560,10 @@ def main():
     achieved_gbs = alg_bytes / (us_attn * 1e-6) / 1e9
     achieved_tflops = alg_flops / (us_attn * 1e-6) / 1e12
     plan_splits = (need > 0)
+    # the long-context and trunk-sharing workloads are bound by the matrix
+    # cores (their arithmetic intensity is far above the ridge point), the
+    # others by HBM bandwidth and latency
+    mfma_bound = args.config in (4, 5)
 
     result = {
         "metric": METRIC,
@@ -578,8 +582,11 @@ def main():
                    "max_prefix_len": w.max_prefix_len, "q_heads": w.num_q_heads,
                    "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
                    "mask": w.mask_kind, "rotating_buffer_sets": R, "hip_graph": True},
-        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
+        "roofline": ({"bound": "mfma", "achieved": achieved_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                      "unit": "TFLOP/s", "frac": achieved_tflops / MFMA_BF16_PEAK_TFLOPS}
+                     if mfma_bound else
+                     {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
+                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS}) | {
                      "traffic": measured_traffic(w.name),
                      "kernel_source_sha256": kernel_source_hash(),
                      "kernel": "tree_verify_attn (attn_bf16_kernel%s)" %
@@ -589,6 +596,8 @@ def main():
         "mfma": {"achieved_tflops": achieved_tflops, "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                  "frac": achieved_tflops / MFMA_BF16_PEAK_TFLOPS,
                  "algorithmic_flops_per_launch": alg_flops},
+        "hbm": {"achieved_gbs": achieved_gbs, "peak_gbs": HBM_PEAK_GBS,
+                "frac": achieved_gbs / HBM_PEAK_GBS},
         "breakdown_us": {"tree_mask_build": us_mask, "tree_verify_attn": us_attn,
                          "tree_accept": us_acc, "step": ms_per_step * 1e3},
         "step_spread_us": spread,
