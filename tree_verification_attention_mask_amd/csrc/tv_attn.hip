@@ -106,12 +106,6 @@ __device__ __forceinline__ float row_max4(float v) {
   return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 
-// Direct-to-LDS 16-byte load of every lane (global_load_lds_dwordx4): lane
-// l's 16 bytes from `src` land at LDS byte address lds + 16 l (lds must be
-// wave-uniform). Issued through inline asm so that the compiler's wait-count
-// insertion does not model it -- it would put a vmcnt(0) before any LDS read
-// of the same array and drain the tile pipeline; the pipeline waits for
-// these loads itself (counted vmcnt, then a barrier). M0 is restored.
 // s_waitcnt operand that waits for nothing (gfx9 encoding: vmcnt bits 3:0
 // and 15:14, expcnt 6:4, lgkmcnt 11:8), and a wait for vmcnt <= N.
 constexpr int W_ALL = (15) | (3 << 14) | (7 << 4) | (15 << 8);
@@ -121,9 +115,49 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((W_ALL & ~0xC00F) | (N & 15) | ((N >> 4) << 14));
 }
 
-__device__ __forceinline__ void lds_dma16(const void* src, const void* lds) {
-  const uint32_t a = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
+// One wave's share of a K or V tile: N direct-to-LDS loads
+// (global_load_lds_dwordx4), load m of lane l reading 16 bytes at
+// base + voff[m] + 1024 m and writing them at LDS byte address
+// lds + 1024 m + 16 l (the instruction's immediate offset adds to both
+// addresses; base and lds are wave-uniform, voff[m] a per-lane 32-bit
+// offset). One M0 setting serves the N loads; M0 is restored after them (the
+// compiler reserves it). Issued through inline asm so that the compiler's
+// wait-count insertion does not model the LDS writes -- it would put a
+// vmcnt(0) before any LDS read of the same arrays and drain the tile
+// pipeline; the pipeline waits for these loads itself (counted vmcnt, then a
+// barrier).
+template <int N>
+__device__ __forceinline__ void dma_burst(const void* base, const uint32_t (&voff)[N], uint32_t lds) {
+  uint32_t saved;
+  if constexpr (N == 4) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %3, %2\n\t"
+        "global_load_lds_dwordx4 %4, %2 offset:1024\n\t"
+        "global_load_lds_dwordx4 %5, %2 offset:2048\n\t"
+        "global_load_lds_dwordx4 %6, %2 offset:3072\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "s"(base), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3])
+        : "memory");
+  } else {
+    static_assert(N == 2, "two or four loads per wave and tile");
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %3, %2\n\t"
+        "global_load_lds_dwordx4 %4, %2 offset:1024\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "s"(base), "v"(voff[0]), "v"(voff[1])
+        : "memory");
+  }
+}
+
+// A single direct-to-LDS load (as dma_burst, N = 1, no step): 16 bytes of
+// every lane from `src` to LDS byte address lds + 16 l.
+__device__ __forceinline__ void dma_single(const void* src, uint32_t lds) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -131,8 +165,13 @@ __device__ __forceinline__ void lds_dma16(const void* src, const void* lds) {
       "global_load_lds_dwordx4 %2, off\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(a), "v"(src)
+      : "s"(lds), "v"(src)
       : "memory");
+}
+
+// LDS byte address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 // XOR swizzle of the 16-byte chunks of K row `row` in LDS: chunk c of the
@@ -149,6 +188,39 @@ __device__ __forceinline__ int kswz(int row) {
   else return row % (D / 8);
 }
 
+// Per-lane byte offsets (less 1 KB per load, as dma_burst adds it) and the
+// LDS byte offset within a stage of load 0, for wave w's share of a tile.
+// Load m of wave w is number ins = w*IPW + m of the tile: ins < K_INS copies
+// K rows [ins*RPI, +RPI) (lane l: row ins*RPI + l/CPR, whose LDS chunk l%CPR
+// receives K chunk (l%CPR) ^ kswz(row)); otherwise V 16-key group
+// j = (ins-K_INS)/VPG, d rows 32*((ins-K_INS)%VPG) + l/2, keys 8*(l%2) .. +7.
+// The first four waves load K, the others V; the loads of one wave cover one
+// whole 16-key group, and pages hold a power of two >= 16 keys, so the group
+// lies in one page: K rows are consecutive 1 KB steps of it, V's d rows step
+// by 32 rows of page_size keys (>= 1 KB).
+template <int D>
+__device__ __forceinline__ void tile_load_offsets(int wave, int lane, int lp, int nw,
+                                                  uint32_t (&voff)[(2 * D / 8) / 8],
+                                                  uint32_t& lds0) {
+  constexpr int K_INS = D / 8, INS = 2 * K_INS, IPW = INS / 8;
+  constexpr int RPI = 512 / D, VPG = D / 32, CPR = D / 8;
+  const bool k_wave = wave < nw / 2;
+#pragma unroll
+  for (int m = 0; m < IPW; ++m) {
+    const int ins = wave * IPW + m;
+    if (k_wave) {
+      const int row = ins * RPI + lane / CPR;
+      voff[m] = 2u * (uint32_t)((lane / CPR) * D + 8 * ((lane % CPR) ^ kswz<D>(row)));
+    } else {
+      const int vi = ins - K_INS, dp = vi % VPG;
+      voff[m] = 2u * (uint32_t)(((32 * dp + lane / 2) << lp) + 8 * (lane % 2)) - 1024u * m;
+    }
+  }
+  const int ins0 = wave * IPW;
+  lds0 = k_wave ? 2u * (uint32_t)(ins0 * RPI * D)
+                : 2u * (uint32_t)(((ins0 - K_INS) / VPG) * 16 * D + 32 * ((ins0 - K_INS) % VPG) * 16);
+}
+
 template <int D, int NW, int RW, bool WIDE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bf16_kernel(Params p) {
@@ -157,7 +229,6 @@ void attn_bf16_kernel(Params p) {
   constexpr int DS = D / 32;           // 32-wide d steps of S^T = K Q^T
   constexpr int DU = D / 16;           // 16-wide d subtiles of O^T
   constexpr int MBLK = 16 * NW * RW;   // rows per workgroup
-  constexpr int CPR = D / 8;           // 16-byte chunks per K row
   constexpr int STAGES = 4;            // LDS ring depth: 3 tiles in flight
   constexpr int TILE_E = kTile * D;    // elements of one K (or V) tile
   constexpr int K_INS = D / 8;         // 1 KB direct-to-LDS loads per K tile
@@ -305,21 +376,20 @@ void attn_bf16_kernel(Params p) {
   __builtin_amdgcn_s_waitcnt(W_ALL & ~0x0F00);
   __syncthreads();
   // Tile [k0, k0+64): skipped when it holds no prefix key and no tree key any
-  // row of the block can see; unmasked when all its keys are visible to all.
-  auto skip_tile = [&](int k0) -> bool {
-    if (!anchor || k0 < P) return false;
-    const int j0 = k0 - P;
-    return j0 > ap_max && j0 + kTile - 1 < br_lo;
-  };
+  // row of the block can see (tree position j0 = k0 - P past every anchor,
+  // j0 + 63 before every branch start); unmasked when all its keys are
+  // visible to all.
   auto full_tile = [&](int k0) -> bool {
     if (k0 + kTile > kv_end) return false;
     if (k0 + kTile <= P) return true;
     return anchor && (k0 + kTile - 1 - P) <= ap_min;
   };
+  // The skipped tiles of the split form one run of consecutive tile starts,
+  // [skip_from, skip_to) (set once the bounds are known; none by default).
+  int skip_from = 0x7fffffff, skip_to = 0x7fffffff;
   auto next_tile = [&](int k0) {
-    int k = k0 + kTile;
-    while (k < ke && skip_tile(k)) k += kTile;
-    return k;
+    const int k = k0 + kTile;
+    return k == skip_from ? skip_to : k;
   };
 
   // Q fragments (B operand of S^T): lane (r16, q4) holds row r16 of its
@@ -411,32 +481,22 @@ void attn_bf16_kernel(Params p) {
   }
   bool rescale = false;  // some row of the wave raised its running max: O *= alpha
 
-  // ---- direct-to-LDS staging (lds_dma16). Load m of wave w is number
-  // ins = w*IPW + m of the tile: ins < K_INS copies K rows [ins*RPI, +RPI)
-  // (lane l: row ins*RPI + l/CPR, whose LDS chunk l%CPR receives K chunk
-  // (l%CPR) ^ kswz(row)); otherwise V 16-key group j = (ins-K_INS)/VPG,
-  // d rows 32*((ins-K_INS)%VPG) + l/2, keys 8*(l%2) .. +7. The first NW/2
-  // waves load K, the others V; either way the loads of one wave cover
-  // GPW whole 16-key groups, gw .. gw+GPW-1, and pages hold a power of two
-  // >= 16 keys, so each group lies in one page: one page id per group and
-  // tile, looked up a step ahead, and a per-lane constant offset.
+  // ---- direct-to-LDS staging (dma_burst, tile_load_offsets): the first
+  // NW/2 waves load K, the others V, one 16-key group (one page segment) of
+  // the tile each; its page id is looked up a step ahead.
   const bool k_wave = wave < NW / 2;
+  // solo blocks (at most 16*NW/2 rows, so group B holds none; the tile loop
+  // below tells how they differ)
+  const bool solo = rows - row0 <= 16 * (NW / 2);
   const int gw = (k_wave ? wave : wave - NW / 2) * GPW;
-  int lane_off[IPW];
-  int lds_off[IPW];  // element offset of the load inside one stage of sK / sV
-#pragma unroll
-  for (int m = 0; m < IPW; ++m) {
-    const int ins = wave * IPW + m;
-    if (k_wave) {
-      const int row = ins * RPI + lane / CPR;
-      lane_off[m] = (lane / CPR) * D + 8 * ((lane % CPR) ^ kswz<D>(row));
-      lds_off[m] = ins * RPI * D;
-    } else {
-      const int vi = ins - K_INS, jj = vi / VPG, dp = vi % VPG;
-      lane_off[m] = ((32 * dp + lane / 2) << lp) + 8 * (lane % 2);
-      lds_off[m] = jj * 16 * D + 32 * dp * 16;
-    }
-  }
+  uint32_t voff[IPW], lds0;
+  tile_load_offsets<D>(wave, lane, lp, NW, voff, lds0);
+  lds0 += k_wave ? lds_u32(&sK[0][0]) : lds_u32(&sV[0][0]);
+  constexpr uint32_t kStageBytes = TILE_E * sizeof(__bf16);
+  // bytes of one (page, kv head) block of K or V, and this head's first one
+  const size_t blk_bytes = (size_t)D * sizeof(__bf16) << lp;
+  const char* kv_g = reinterpret_cast<const char*>(k_wave ? p.k : p.v) + (size_t)g * blk_bytes;
+  const size_t pg_stride = blk_bytes * p.hkv;
   const int last = kv_end - 1;
   // page id (wave-uniform) of tile position pos; positions past the
   // request's last key use the last key's page: tiles past the end read
@@ -464,22 +524,21 @@ void attn_bf16_kernel(Params p) {
     for (int l = 0; l < GPW; ++l) pg[l] = __builtin_amdgcn_readfirstlane(pg_raw[l]);
   };
   auto issue = [&](int stage, int k0, const int (&pg)[GPW]) {
-    if (k_wave) {
+    // the wave's group starts at position slot of its page (K rows of D
+    // elements, V 16-key runs of each d row)
+    const int slot = (k0 + 16 * gw) & pmask;
+    const char* src = kv_g + (size_t)(uint32_t)pg[0] * pg_stride +
+                      (uint32_t)(k_wave ? slot * D : slot) * sizeof(__bf16);
+    const uint32_t lds = lds0 + (uint32_t)stage * kStageBytes;
+    if (solo) {
+      // blocks bound by HBM latency: the wave's loads one at a time, each
+      // with its own M0 (four back-to-back loads were slower there, 102.9
+      // against 99.2 us for 64 short chains; the blocks of both groups gain
+      // from the burst's fewer scalar instructions)
 #pragma unroll
-      for (int m = 0; m < IPW; ++m) {
-        const int l = (m * RPI) / 16;
-        const int slot0 = (k0 + 16 * (gw + l) + (m * RPI) % 16) & pmask;
-        const long blk = (long)pg[l] * p.hkv + g;
-        lds_dma16(p.k + (((blk << lp) + slot0) * D + lane_off[m]), &sK[stage][lds_off[m]]);
-      }
+      for (int m = 0; m < IPW; ++m) dma_single(src + voff[m] + 1024 * m, lds + 1024 * m);
     } else {
-#pragma unroll
-      for (int m = 0; m < IPW; ++m) {
-        const int l = m / VPG;
-        const int slot0 = (k0 + 16 * (gw + l)) & pmask;
-        const long blk = (long)pg[l] * p.hkv + g;
-        lds_dma16(p.v + (((blk * D) << lp) + slot0 + lane_off[m]), &sV[stage][lds_off[m]]);
-      }
+      dma_burst<IPW>(src, voff, lds);
     }
   };
 
@@ -693,9 +752,17 @@ void attn_bf16_kernel(Params p) {
     }
     __syncthreads();
     ap_min = s_bounds[0]; ap_max = s_bounds[1]; br_lo = s_bounds[2];
+    // tile starts ks + 64j skipped: from the first at or past
+    // max(P, P + ap_max + 1) up to the last at or before P + br_lo - 64
+    const long long lo = max((long long)P, (long long)P + ap_max + 1);
+    const long long hi = (long long)P + br_lo - kTile;
+    const long long f = ks + ((max(lo - ks, 0LL) + kTile - 1) / kTile) * kTile;
+    if (f <= hi && f < ke) {
+      skip_from = (int)f;
+      skip_to = (int)min((long long)ks + ((hi - ks) / kTile + 1) * kTile, (long long)ke);
+    }
   }
-  int c_cur = ks;
-  while (c_cur < ke && skip_tile(c_cur)) c_cur += kTile;
+  int c_cur = ks == skip_from ? skip_to : ks;
   int c_prev = ke;  // tile m-1 (none yet)
   int c_n1 = next_tile(c_cur), c_n2 = next_tile(c_n1);
   if (min(c_cur, ke) != spec0 || min(c_n1, ke) != spec1) {
@@ -711,7 +778,6 @@ void attn_bf16_kernel(Params p) {
   // slot 2m ends. Tiles are then requested three ahead, in slot 2m+1, into
   // that stage (3 tiles in flight instead of 2: these blocks are bound by
   // HBM latency, not by the matrix cores).
-  const bool solo = rows - row0 <= 16 * (NW / 2);
   int c_n3 = solo ? next_tile(c_n2) : ke;  // tile to request in slot 2m+1 (solo)
   // Q fragments and mask rows are used from registers from here on (this
   // waits for them, and for the tiles requested above)
@@ -874,7 +940,6 @@ void attn_bf16_short_kernel(Params p) {
   constexpr int DS = D / 32;           // 32-wide d steps of S^T = K Q^T
   constexpr int DU = D / 16;           // 16-wide d subtiles of O^T
   constexpr int MBLK = 16 * NW;        // rows per workgroup
-  constexpr int CPR = D / 8;           // 16-byte chunks per K row
   constexpr int TILE_E = kTile * D;
   constexpr int K_INS = D / 8;         // 1 KB direct-to-LDS loads per K tile
   constexpr int INS = 2 * K_INS;
@@ -950,37 +1015,19 @@ void attn_bf16_short_kernel(Params p) {
                                            p.q + (size_t)orow * D + 32 * s + 8 * q4));
 
   // ---- all tiles of the split, straight into LDS (layouts as in the tile loop)
-  int lane_off[IPW], lds_off[IPW];
-#pragma unroll
-  for (int m = 0; m < IPW; ++m) {
-    const int ins = wave * IPW + m;
-    if (k_wave) {
-      const int row_k = ins * RPI + lane / CPR;
-      lane_off[m] = (lane / CPR) * D + 8 * ((lane % CPR) ^ kswz<D>(row_k));
-      lds_off[m] = ins * RPI * D;
-    } else {
-      const int vi = ins - K_INS, jj = vi / VPG, dp = vi % VPG;
-      lane_off[m] = ((32 * dp + lane / 2) << lp) + 8 * (lane % 2);
-      lds_off[m] = jj * 16 * D + 32 * dp * 16;
-    }
-  }
+  uint32_t voff[IPW], lds0;
+  tile_load_offsets<D>(wave, lane, lp, NW, voff, lds0);
+  lds0 += k_wave ? lds_u32(&sK[0][0]) : lds_u32(&sV[0][0]);
+  const size_t blk_bytes = (size_t)D * sizeof(__bf16) << lp;
+  const char* kv_g = reinterpret_cast<const char*>(k_wave ? p.k : p.v) + (size_t)g * blk_bytes;
 #pragma unroll
   for (int t = 0; t < kShortTiles; ++t) {
     if (t >= nt) break;
-    const int k0 = ks + kTile * t;
-    const long blk = (long)clampi(pg[t], 0, p.num_pages - 1) * p.hkv + g;
-    if (k_wave) {
-#pragma unroll
-      for (int m = 0; m < IPW; ++m) {
-        const int slot0 = (k0 + 16 * gw + m * RPI) & pmask;
-        lds_dma16(p.k + (((blk << lp) + slot0) * D + lane_off[m]), &sK[t][lds_off[m]]);
-      }
-    } else {
-      const int slot0 = (k0 + 16 * gw) & pmask;
-#pragma unroll
-      for (int m = 0; m < IPW; ++m)
-        lds_dma16(p.v + (((blk * D) << lp) + slot0 + lane_off[m]), &sV[t][lds_off[m]]);
-    }
+    const int slot = (ks + kTile * t + 16 * gw) & pmask;
+    const uint32_t pgt = __builtin_amdgcn_readfirstlane(clampi(pg[t], 0, p.num_pages - 1));
+    const char* src = kv_g + (size_t)pgt * (blk_bytes * p.hkv) +
+                      (uint32_t)(k_wave ? slot * D : slot) * sizeof(__bf16);
+    dma_burst<IPW>(src, voff, lds0 + (uint32_t)(t * TILE_E * sizeof(__bf16)));
   }
   // Q and mask rows are used from registers from here on
 #pragma unroll
