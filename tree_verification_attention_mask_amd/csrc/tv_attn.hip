@@ -668,7 +668,8 @@ void attn_bf16_kernel(Params p) {
   };
   // zero the V columns of positions past the request's last key in a tile
   // that just landed (their K columns are masked; V must hold finite zeros
-  // for P = 0 to contribute nothing); the next barrier publishes them
+  // for P = 0 to contribute nothing); the next barrier publishes them (the
+  // first reader of V(m) is M(m+1), after the next step's first barrier)
   auto zero_tail = [&](int stage, int k0) {
     if (k0 + kTile <= kv_end) return;
     const int lim = kv_end - k0;  // tile keys >= lim are past the end
@@ -812,6 +813,17 @@ void attn_bf16_kernel(Params p) {
       pages_load(c_nn);
     }
   };
+  // The barrier between a step's two slots orders LDS only in solo blocks:
+  // there the stage of tile m-1, which group A's M(m) reads, takes tile m+3
+  // in slot 2m+1 (and the V waves of group B issue part of it). Otherwise
+  // every stage a step writes was last read in an earlier step and every
+  // tile it reads landed before the step's first barrier, so the two groups
+  // run their clusters back to back: one wave's matrix cluster meets the
+  // other's VALU cluster without either waiting for the slower side of each
+  // slot.
+  auto mid_barrier = [&]() {
+    if (solo) barrier();
+  };
   auto mid = [&]() {  // after the barrier that opens slot 2m+1
     if (solo) {
       if (c_n3 < ke) issue((m + 3) & (STAGES - 1), c_n3, pgn);
@@ -828,12 +840,12 @@ void attn_bf16_kernel(Params p) {
   };
   // Each group runs a straight loop (no per-slot branch between the two
   // clusters, which would force copies of the accumulators); both execute
-  // 2 barriers per tile plus 2 at the end.
+  // 1 barrier per tile plus 1 at the end (2 and 2 in solo blocks).
   if (!grp_b) {
     while (c_cur < ke) {
       head();
       cluster_m(m);
-      barrier();
+      mid_barrier();
       mid();
       request();
       cluster_v(c_cur);
@@ -842,12 +854,12 @@ void attn_bf16_kernel(Params p) {
     head();
     request();
     cluster_m(m);  // PV of the last tile
-    barrier();
+    mid_barrier();
   } else {
     if (c_cur < ke) {
       head();
       request();
-      barrier();
+      mid_barrier();
       mid();
       cluster_m(m);
       advance();
@@ -856,7 +868,7 @@ void attn_bf16_kernel(Params p) {
       head();
       request();
       cluster_v(c_prev);
-      barrier();
+      mid_barrier();
       mid();
       cluster_m(m);
       advance();
@@ -864,7 +876,7 @@ void attn_bf16_kernel(Params p) {
     head();
     request();
     if (c_prev < ke) cluster_v(c_prev);
-    barrier();
+    mid_barrier();
     cluster_m(m);  // PV of the last tile
   }
 
