@@ -53,6 +53,10 @@ constexpr int kTile = 64;     // keys per tile
 constexpr int kMaxSplitPages = 4096;  // page ids one workgroup can stage (16-token pages: 64K keys)
 constexpr int kMaxLptBatch = 256;   // requests the in-kernel longest-first order handles
 constexpr float kLazyMax = 8.f;      // running-max slack before O is rescaled (log2 units)
+// running max (log2 units) of a row before its first visible key: finite, so
+// that the probabilities' offset needs no select, and far below any score
+// (the first key raises it, with a rescale of the still-zero O and l by 0)
+constexpr float kNoMax = -1e30f;
 
 struct Params {
   const __bf16* q;
@@ -98,12 +102,20 @@ __device__ __forceinline__ float row_sum4(float v) {
   swap_pair(__builtin_bit_cast(uint32_t, v), false, a, b);
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
+// v_max_f32 of two lanes' values: fmaxf on values the compiler received as
+// integer bits would first quiet each operand (two more v_max_f32); the
+// scores are never signalling NaNs
+__device__ __forceinline__ float fmax_bits(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float row_max4(float v) {
   uint32_t a, b;
   swap_pair(__builtin_bit_cast(uint32_t, v), true, a, b);
-  v = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  v = fmax_bits(a, b);
   swap_pair(__builtin_bit_cast(uint32_t, v), false, a, b);
-  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  return fmax_bits(a, b);
 }
 
 // s_waitcnt operand that waits for nothing (gfx9 encoding: vmcnt bits 3:0
@@ -379,11 +391,10 @@ void attn_bf16_kernel(Params p) {
   // row of the block can see (tree position j0 = k0 - P past every anchor,
   // j0 + 63 before every branch start); unmasked when all its keys are
   // visible to all.
-  auto full_tile = [&](int k0) -> bool {
-    if (k0 + kTile > kv_end) return false;
-    if (k0 + kTile <= P) return true;
-    return anchor && (k0 + kTile - 1 - P) <= ap_min;
-  };
+  // (unmasked: its keys lie before full_end = min(kv_end, P), or with the
+  // ANCHOR form min(kv_end, max(P, P + ap_min + 1)), set with the bounds)
+  int full_end = min(kv_end, P);
+  auto full_tile = [&](int k0) -> bool { return k0 + kTile <= full_end; };
   // The skipped tiles of the split form one run of consecutive tile starts,
   // [skip_from, skip_to) (set once the bounds are known; none by default).
   int skip_from = 0x7fffffff, skip_to = 0x7fffffff;
@@ -473,7 +484,7 @@ void attn_bf16_kernel(Params p) {
   float m_run[RW], alpha[RW];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
-    m_run[r] = -INFINITY;
+    m_run[r] = kNoMax;
     l_lane[r] = 0.f;
     alpha[r] = 1.f;
 #pragma unroll
@@ -586,7 +597,7 @@ void attn_bf16_kernel(Params p) {
   // their O rescaled; probabilities stay <= 2^kLazyMax, exact in fp32 and
   // rounded to bf16 with the same relative error as any other value.
   auto row_update = [&](f32x4 (&sacc)[RW][4]) {
-    bool need = false;
+    bool up_any = false;
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
       float mx = -INFINITY;
@@ -597,16 +608,16 @@ void attn_bf16_kernel(Params p) {
       mx = row_max4(mx) * p.scale_log2;
       const bool up = mx > m_run[r] + kLazyMax;
       alpha[r] = up ? __builtin_amdgcn_exp2f(m_run[r] - mx) : 1.f;
-      need = need || (up && m_run[r] != -INFINITY);
       m_run[r] = up ? mx : m_run[r];
+      up_any = up_any || up;
     }
-    rescale = __any(need);
+    rescale = __builtin_amdgcn_ballot_w64(up_any) != 0;
   };
   // ---- probabilities of a tile (bf16 B operand of the PV product)
   auto probs = [&](f32x4 (&sacc)[RW][4], bf16x8 (&pf)[RW][2]) {
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
-      const float m_use = (m_run[r] == -INFINITY) ? 0.f : m_run[r];
+      const float m_use = m_run[r];
       float part[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -753,6 +764,7 @@ void attn_bf16_kernel(Params p) {
     }
     __syncthreads();
     ap_min = s_bounds[0]; ap_max = s_bounds[1]; br_lo = s_bounds[2];
+    full_end = (int)min((long long)kv_end, max((long long)P, (long long)P + ap_min + 1));
     // tile starts ks + 64j skipped: from the first at or past
     // max(P, P + ap_max + 1) up to the last at or before P + br_lo - 64
     const long long lo = max((long long)P, (long long)P + ap_max + 1);
@@ -912,7 +924,7 @@ void attn_bf16_kernel(Params p) {
         __builtin_nontemporal_store(h, reinterpret_cast<bf16x4*>(p.part_o + prow * D + 16 * u + 4 * q4));
       }
       if (q4 == 0) {
-        __builtin_nontemporal_store(m_run[r], p.part_ml + prow * 2);
+        __builtin_nontemporal_store(l_run[r] > 0.f ? m_run[r] : -INFINITY, p.part_ml + prow * 2);
         __builtin_nontemporal_store(l_run[r], p.part_ml + prow * 2 + 1);
       }
     }
