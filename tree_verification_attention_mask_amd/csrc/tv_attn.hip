@@ -102,12 +102,23 @@ __device__ __forceinline__ float row_sum4(float v) {
   swap_pair(__builtin_bit_cast(uint32_t, v), false, a, b);
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
-// v_max_f32 of two lanes' values: fmaxf on values the compiler received as
-// integer bits would first quiet each operand (two more v_max_f32); the
-// scores are never signalling NaNs
+// v_max_f32 / v_max3_f32 as written: fmaxf on values the compiler cannot
+// prove quiet (integer bits from a lane swap, masked accumulators) first
+// quiets each operand with one more v_max_f32; the scores are never
+// signalling NaNs
 __device__ __forceinline__ float fmax_bits(uint32_t a, uint32_t b) {
   float r;
   asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float fmax_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float fmax3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
 __device__ __forceinline__ float row_max4(float v) {
@@ -598,14 +609,22 @@ void attn_bf16_kernel(Params p) {
   // rounded to bf16 with the same relative error as any other value.
   auto row_update = [&](f32x4 (&sacc)[RW][4]) {
     bool up_any = false;
+    // each lane's max of its 16 scores of a row subtile as a tree of v_max3
+    // (depth 3 instead of a chain of 8), the row subtiles side by side
+    float mx4[RW];
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
-      float mx = -INFINITY;
+      const f32x4* v = sacc[r];
+      const float a0 = fmax3_raw(v[0][0], v[0][1], v[0][2]);
+      const float a1 = fmax3_raw(v[0][3], v[1][0], v[1][1]);
+      const float a2 = fmax3_raw(v[1][2], v[1][3], v[2][0]);
+      const float a3 = fmax3_raw(v[2][1], v[2][2], v[2][3]);
+      const float a4 = fmax3_raw(v[3][0], v[3][1], v[3][2]);
+      mx4[r] = fmax_raw(fmax3_raw(a0, a1, a2), fmax3_raw(a3, a4, v[3][3]));
+    }
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[r][t][i]);
-      mx = row_max4(mx) * p.scale_log2;
+    for (int r = 0; r < RW; ++r) {
+      const float mx = row_max4(mx4[r]) * p.scale_log2;
       const bool up = mx > m_run[r] + kLazyMax;
       alpha[r] = up ? __builtin_amdgcn_exp2f(m_run[r] - mx) : 1.f;
       m_run[r] = up ? mx : m_run[r];
