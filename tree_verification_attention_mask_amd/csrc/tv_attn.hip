@@ -869,10 +869,38 @@ void attn_bf16_kernel(Params p) {
     c_prev = c_cur; c_cur = c_n1; c_n1 = c_n2; c_n2 = n2; c_n3 = n3;
     ++m;
   };
-  // Each group runs a straight loop (no per-slot branch between the two
+  // Steady state of blocks of both groups (tiles m, m+1 and m+2 exist):
+  // tile m is full (it ends before tile m+2 starts, at most at the last
+  // key), so the step needs no tail zeros, and its wait count, request and
+  // successor are fixed -- the scalar code between the clusters stays short.
+  auto head_ss = [&]() {
+    wait_vmem<IPW>();
+    barrier();
+  };
+  auto request_ss = [&]() {
+    issue((m + 2) & (STAGES - 1), c_n2, pgn);
+    c_nn = next_tile(c_n2);
+    pages_load(c_nn);
+  };
+  auto advance_ss = [&]() {
+    pages_take(pgn);
+    c_prev = c_cur; c_cur = c_n1; c_n1 = c_n2; c_n2 = c_nn;
+    ++m;
+  };
+  // Each group runs straight loops (no per-slot branch between the two
   // clusters, which would force copies of the accumulators); both execute
-  // 1 barrier per tile plus 1 at the end (2 and 2 in solo blocks).
+  // 1 barrier per tile plus 1 at the end (2 and 2 in solo blocks), so the
+  // steady-state loop and the general one may hand over at any step.
   if (!grp_b) {
+    if (!solo) {
+      while (c_n2 < ke) {
+        head_ss();
+        cluster_m(m);
+        request_ss();
+        cluster_v(c_cur);
+        advance_ss();
+      }
+    }
     while (c_cur < ke) {
       head();
       cluster_m(m);
@@ -894,6 +922,15 @@ void attn_bf16_kernel(Params p) {
       mid();
       cluster_m(m);
       advance();
+    }
+    if (!solo) {
+      while (c_n2 < ke) {
+        head_ss();
+        request_ss();
+        cluster_v(c_prev);
+        cluster_m(m);
+        advance_ss();
+      }
     }
     while (c_cur < ke) {
       head();
