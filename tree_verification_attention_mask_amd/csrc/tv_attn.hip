@@ -268,7 +268,7 @@ void attn_bf16_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) __bf16 sK[STAGES][TILE_E];
   __shared__ __attribute__((aligned(16))) __bf16 sV[STAGES][TILE_E];
   __shared__ int s_pages[kMaxSplitPages];  // page ids of this block's key window
-  __shared__ int s_bounds[4];
+  __shared__ int s_bounds[NW][4];  // ANCHOR form: each wave's partial bounds
   __shared__ int s_len[kMaxLptBatch], s_order[kMaxLptBatch];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -380,22 +380,44 @@ void attn_bf16_kernel(Params p) {
   // node is visible to any of its rows.
   const int node_hi = min(n - 1, (row0 + MBLK - 1) / G);
   const int ke = min(min(ks + p.keys_per_split, kv_end), P + node_hi + 1);
+
+  // ANCHOR form: block-wide bounds to skip tree tiles no row can see and to
+  // treat tiles every row sees in full as unmasked: the min and max anchor
+  // and the lowest branch start over the block's nodes. Their loads go out
+  // here, behind only the page-table loads that the barrier below waits for
+  // anyway and ahead of every Q, mask-row and tile load (loads return in
+  // order: a bound loaded after the tile requests would wait for the tiles).
+  // Each wave folds its nodes with a butterfly; the barrier publishes the
+  // waves' partial bounds.
+  int ap_min = -1, ap_max = 0x7fffffff, br_lo = 0x7fffffff;
+  const bool anchor = p.mask.kind == TV_MASK_ANCHOR;
+  if (anchor) {
+    const int node_lo = row0 / G;
+    int a_min = 0x7fffffff, a_max = -1, b_lo = 0x7fffffff;
+    for (int i = node_lo + tid; i <= node_hi; i += T) {
+      const int a = p.mask.anchor_pos[n0 + i], d = p.mask.branch_depth[n0 + i];
+      a_min = min(a_min, a);
+      a_max = max(a_max, a);
+      if (d > 0) b_lo = min(b_lo, i - d + 1);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      a_min = min(a_min, __shfl_xor(a_min, off, 64));
+      a_max = max(a_max, __shfl_xor(a_max, off, 64));
+      b_lo = min(b_lo, __shfl_xor(b_lo, off, 64));
+    }
+    if (lane == 0) { s_bounds[wave][0] = a_min; s_bounds[wave][1] = a_max; s_bounds[wave][2] = b_lo; }
+  }
 #pragma unroll
   for (int j = 0; j < PPT; ++j) {
     const int i = tid + j * T;
     if (i < n_pg) s_pages[i] = clampi(pgv[j], 0, p.num_pages - 1);
   }
-
-  // ANCHOR form: block-wide bounds to skip tree tiles no row can see and to
-  // treat tiles every row sees in full as unmasked.
-  int ap_min = -1, ap_max = 0x7fffffff, br_lo = 0x7fffffff;
-  const bool anchor = p.mask.kind == TV_MASK_ANCHOR;
-  if (anchor && tid == 0) { s_bounds[0] = 0x7fffffff; s_bounds[1] = -1; s_bounds[2] = 0x7fffffff; }
   // V of stage STAGES-1 is read (times P = 0) by the first M cluster
   for (int c = tid; c < TILE_E / 8; c += T)
     reinterpret_cast<uint4*>(&sV[STAGES - 1][0])[c] = uint4{0u, 0u, 0u, 0u};
-  // the page list, the bounds' initial values and the zeros are written;
-  // make them visible
+  // the page list, the partial bounds and the zeros are written; make them
+  // visible (the loads this waits for are the page table's and the bounds')
   __builtin_amdgcn_s_waitcnt(W_ALL & ~0x0F00);
   __syncthreads();
   // Tile [k0, k0+64): skipped when it holds no prefix key and no tree key any
@@ -413,6 +435,30 @@ void attn_bf16_kernel(Params p) {
     const int k = k0 + kTile;
     return k == skip_from ? skip_to : k;
   };
+  if (anchor) {
+    int a_min = 0x7fffffff, a_max = -1, b_lo = 0x7fffffff;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      a_min = min(a_min, s_bounds[w][0]);
+      a_max = max(a_max, s_bounds[w][1]);
+      b_lo = min(b_lo, s_bounds[w][2]);
+    }
+    ap_min = a_min; ap_max = a_max; br_lo = b_lo;
+    full_end = (int)min((long long)kv_end, max((long long)P, (long long)P + ap_min + 1));
+    // tile starts ks + 64j skipped: from the first at or past
+    // max(P, P + ap_max + 1) up to the last at or before P + br_lo - 64
+    const long long lo = max((long long)P, (long long)P + ap_max + 1);
+    const long long hi = (long long)P + br_lo - kTile;
+    const long long f = ks + ((max(lo - ks, 0LL) + kTile - 1) / kTile) * kTile;
+    if (f <= hi && f < ke) {
+      skip_from = (int)f;
+      skip_to = (int)min((long long)ks + ((hi - ks) / kTile + 1) * kTile, (long long)ke);
+    }
+  }
+  // the block's first tiles (known before any tile is requested)
+  int c_cur = ks == skip_from ? skip_to : ks;
+  int c_prev = ke;  // tile m-1 (none yet)
+  int c_n1 = next_tile(c_cur), c_n2 = next_tile(c_n1);
 
   // Q fragments (B operand of S^T): lane (r16, q4) holds row r16 of its
   // subtile, d = 32s + 8q4 .. +7. Subtiles st = wave + NW r hold rows
@@ -760,51 +806,11 @@ void attn_bf16_kernel(Params p) {
     probs(sc, pf);
   };
 
-  // The split's first two tiles are requested before the block's anchor
-  // bounds are known, while those loads and the Q and mask-row loads are in
-  // flight (one dependent round trip fewer; under load each costs a few us).
-  // Only the anchor form skips tiles, and its first tile ks is skipped only
-  // in a split that starts in the tree part past every anchor: then the
-  // tiles are requested again once the bounds are known.
-  const int spec0 = ks < ke ? ks : ke;
-  const int spec1 = spec0 + kTile < ke ? spec0 + kTile : ke;
+  // The block's first two tiles, requested right after the Q and mask-row
+  // loads (the bounds that decide them are already known).
   int pgn[GPW];
-  if (spec0 < ke) { pages_for(spec0, pgn); issue(0, spec0, pgn); }
-  if (spec1 < ke) { pages_for(spec1, pgn); issue(1, spec1, pgn); }
-  if (anchor) {
-    // ANCHOR form: block-wide bounds to skip tree tiles no row can see and
-    // to treat tiles every row sees in full as unmasked
-    const int node_lo = row0 / G;
-    for (int i = node_lo + tid; i <= node_hi; i += T) {
-      const int a = p.mask.anchor_pos[n0 + i], d = p.mask.branch_depth[n0 + i];
-      atomicMin(&s_bounds[0], a);
-      atomicMax(&s_bounds[1], a);
-      if (d > 0) atomicMin(&s_bounds[2], i - d + 1);
-    }
-    __syncthreads();
-    ap_min = s_bounds[0]; ap_max = s_bounds[1]; br_lo = s_bounds[2];
-    full_end = (int)min((long long)kv_end, max((long long)P, (long long)P + ap_min + 1));
-    // tile starts ks + 64j skipped: from the first at or past
-    // max(P, P + ap_max + 1) up to the last at or before P + br_lo - 64
-    const long long lo = max((long long)P, (long long)P + ap_max + 1);
-    const long long hi = (long long)P + br_lo - kTile;
-    const long long f = ks + ((max(lo - ks, 0LL) + kTile - 1) / kTile) * kTile;
-    if (f <= hi && f < ke) {
-      skip_from = (int)f;
-      skip_to = (int)min((long long)ks + ((hi - ks) / kTile + 1) * kTile, (long long)ke);
-    }
-  }
-  int c_cur = ks == skip_from ? skip_to : ks;
-  int c_prev = ke;  // tile m-1 (none yet)
-  int c_n1 = next_tile(c_cur), c_n2 = next_tile(c_n1);
-  if (min(c_cur, ke) != spec0 || min(c_n1, ke) != spec1) {
-    // the bounds skip a requested tile: let the requests land, then ask for
-    // the right ones (a workgroup-uniform branch)
-    wait_vmem<0>();
-    barrier();
-    if (c_cur < ke) { pages_for(c_cur, pgn); issue(0, c_cur, pgn); }
-    if (c_n1 < ke) { pages_for(c_n1, pgn); issue(1, c_n1, pgn); }
-  }
+  if (c_cur < ke) { pages_for(c_cur, pgn); issue(0, c_cur, pgn); }
+  if (c_n1 < ke) { pages_for(c_n1, pgn); issue(1, c_n1, pgn); }
   // Solo blocks: the waves of group B hold no rows (at most 16*NW/2 rows),
   // so only group A reads the tiles and the stage of tile m-1 is free once
   // slot 2m ends. Tiles are then requested three ahead, in slot 2m+1, into
