@@ -345,13 +345,11 @@ void attn_bf16_kernel(Params p) {
   const int pg_lo = ks >> lp;
   const int n_pg = max(1, min(((ks + p.keys_per_split + kTile - 1) >> lp) - pg_lo + 1, kMaxSplitPages));
   int pgv[PPT];
-  {
-    const int32_t* row_tab = p.block_table + (size_t)b * p.max_pages;
+  const int32_t* row_tab = p.block_table + (size_t)b * p.max_pages;
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const int i = tid + j * T;
-      pgv[j] = (i < n_pg) ? row_tab[min(pg_lo + i, p.max_pages - 1)] : 0;
-    }
+  for (int j = 0; j < PPT; ++j) {
+    const int i = tid + j * T;
+    pgv[j] = (i < n_pg) ? row_tab[min(pg_lo + i, p.max_pages - 1)] : 0;
   }
 
   const int n0 = clampi(p.cu_nodes[b], 0, p.total_nodes);
@@ -391,163 +389,6 @@ void attn_bf16_kernel(Params p) {
   // waves' partial bounds.
   int ap_min = -1, ap_max = 0x7fffffff, br_lo = 0x7fffffff;
   const bool anchor = p.mask.kind == TV_MASK_ANCHOR;
-  if (anchor) {
-    const int node_lo = row0 / G;
-    int a_min = 0x7fffffff, a_max = -1, b_lo = 0x7fffffff;
-    for (int i = node_lo + tid; i <= node_hi; i += T) {
-      const int a = p.mask.anchor_pos[n0 + i], d = p.mask.branch_depth[n0 + i];
-      a_min = min(a_min, a);
-      a_max = max(a_max, a);
-      if (d > 0) b_lo = min(b_lo, i - d + 1);
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      a_min = min(a_min, __shfl_xor(a_min, off, 64));
-      a_max = max(a_max, __shfl_xor(a_max, off, 64));
-      b_lo = min(b_lo, __shfl_xor(b_lo, off, 64));
-    }
-    if (lane == 0) { s_bounds[wave][0] = a_min; s_bounds[wave][1] = a_max; s_bounds[wave][2] = b_lo; }
-  }
-#pragma unroll
-  for (int j = 0; j < PPT; ++j) {
-    const int i = tid + j * T;
-    if (i < n_pg) s_pages[i] = clampi(pgv[j], 0, p.num_pages - 1);
-  }
-  // V of stage STAGES-1 is read (times P = 0) by the first M cluster
-  for (int c = tid; c < TILE_E / 8; c += T)
-    reinterpret_cast<uint4*>(&sV[STAGES - 1][0])[c] = uint4{0u, 0u, 0u, 0u};
-  // the page list, the partial bounds and the zeros are written; make them
-  // visible (the loads this waits for are the page table's and the bounds')
-  __builtin_amdgcn_s_waitcnt(W_ALL & ~0x0F00);
-  __syncthreads();
-  // Tile [k0, k0+64): skipped when it holds no prefix key and no tree key any
-  // row of the block can see (tree position j0 = k0 - P past every anchor,
-  // j0 + 63 before every branch start); unmasked when all its keys are
-  // visible to all.
-  // (unmasked: its keys lie before full_end = min(kv_end, P), or with the
-  // ANCHOR form min(kv_end, max(P, P + ap_min + 1)), set with the bounds)
-  int full_end = min(kv_end, P);
-  auto full_tile = [&](int k0) -> bool { return k0 + kTile <= full_end; };
-  // The skipped tiles of the split form one run of consecutive tile starts,
-  // [skip_from, skip_to) (set once the bounds are known; none by default).
-  int skip_from = 0x7fffffff, skip_to = 0x7fffffff;
-  auto next_tile = [&](int k0) {
-    const int k = k0 + kTile;
-    return k == skip_from ? skip_to : k;
-  };
-  if (anchor) {
-    int a_min = 0x7fffffff, a_max = -1, b_lo = 0x7fffffff;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      a_min = min(a_min, s_bounds[w][0]);
-      a_max = max(a_max, s_bounds[w][1]);
-      b_lo = min(b_lo, s_bounds[w][2]);
-    }
-    ap_min = a_min; ap_max = a_max; br_lo = b_lo;
-    full_end = (int)min((long long)kv_end, max((long long)P, (long long)P + ap_min + 1));
-    // tile starts ks + 64j skipped: from the first at or past
-    // max(P, P + ap_max + 1) up to the last at or before P + br_lo - 64
-    const long long lo = max((long long)P, (long long)P + ap_max + 1);
-    const long long hi = (long long)P + br_lo - kTile;
-    const long long f = ks + ((max(lo - ks, 0LL) + kTile - 1) / kTile) * kTile;
-    if (f <= hi && f < ke) {
-      skip_from = (int)f;
-      skip_to = (int)min((long long)ks + ((hi - ks) / kTile + 1) * kTile, (long long)ke);
-    }
-  }
-  // the block's first tiles (known before any tile is requested)
-  int c_cur = ks == skip_from ? skip_to : ks;
-  int c_prev = ke;  // tile m-1 (none yet)
-  int c_n1 = next_tile(c_cur), c_n2 = next_tile(c_n1);
-
-  // Q fragments (B operand of S^T): lane (r16, q4) holds row r16 of its
-  // subtile, d = 32s + 8q4 .. +7. Subtiles st = wave + NW r hold rows
-  // row0 + 16 st ..; the first nv of them (a wave-uniform count) have a real
-  // row. Padding rows carry the request's first row's Q and are never
-  // stored, so the MFMAs below run unguarded. These loads, and the mask
-  // rows', stay in flight while the first K/V tiles are requested.
-  int nv = 0;
-#pragma unroll
-  for (int r = 0; r < RW; ++r) nv += (row0 + 16 * (wave + NW * r) < rows) ? 1 : 0;
-  bf16x8 qf[RW][DS];
-  int orow[RW], rnode[RW], rloc[RW];
-  bool row_ok[RW];
-  // per-row mask data kept in registers: ANCHOR (anchor_pos | branch_depth
-  // << 32 in m_w0), BITS with <= 2 words (the two words in m_w0, m_w1);
-  // wider BITS masks (the WIDE instantiation) are read per masked tile
-  const bool bits_in_regs = !WIDE && !anchor;
-  uint64_t m_w0[RW], m_w1[RW];
-#pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    const int row = row0 + 16 * (wave + NW * r) + r16;
-    row_ok[r] = row < rows;
-    const int i = row_ok[r] ? row / G : 0;
-    const int hl = row_ok[r] ? row % G : 0;
-    rloc[r] = i;
-    rnode[r] = n0 + i;
-    orow[r] = (n0 + i) * p.hq + g * G + hl;
-    // unconditional loads whose values are first used after the first tiles
-    // are requested: a padding row reads the request's first row (its scores
-    // are computed, never stored, and no other row depends on them; its mask
-    // is never consulted), and no select on the loaded values here, which
-    // would wait for them before the tile requests. With one mask word the
-    // second load reads the first again; bits past the last node are cut by
-    // the request's key range.
-    m_w0[r] = 0ull; m_w1[r] = 0ull;
-    if (anchor) {
-      m_w0[r] = (uint64_t)(uint32_t)p.mask.anchor_pos[rnode[r]] |
-                ((uint64_t)(uint32_t)p.mask.branch_depth[rnode[r]] << 32);
-    } else if (bits_in_regs) {
-      m_w0[r] = p.mask.bits[(size_t)rnode[r] * p.mask.words];
-      m_w1[r] = p.mask.bits[(size_t)rnode[r] * p.mask.words + (p.mask.words - 1)];
-    }
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      const uint4 u = *reinterpret_cast<const uint4*>(p.q + (size_t)orow[r] * D + 32 * s + 8 * q4);
-      qf[r][s] = __builtin_bit_cast(bf16x8, u);
-    }
-  }
-  // Visibility of keys [k0, k0 + 64) for this lane's row of subtile r.
-  auto row_visibility = [&](int r, int k0) -> uint64_t {
-    if (!row_ok[r]) return 0ull;
-    uint64_t v = range_bits(0, P - 1 - k0);
-    if (k0 + kTile > P && k0 < kv_end) {
-      const int j0 = k0 - P;  // > -64
-      uint64_t t;
-      if (anchor) {
-        const int ap = (int)(uint32_t)m_w0[r], bd = (int)(uint32_t)(m_w0[r] >> 32);
-        t = range_bits(-j0, ap - j0) | range_bits(rloc[r] - bd + 1 - j0, rloc[r] - j0);
-      } else if (!WIDE) {
-        if (j0 < 0) {
-          t = m_w0[r] << (-j0);
-        } else {
-          const int sh = j0 & 63;
-          const uint64_t lo = (j0 < 64) ? m_w0[r] : m_w1[r];
-          const uint64_t hi = (j0 < 64) ? m_w1[r] : 0ull;
-          t = sh ? ((lo >> sh) | (hi << (64 - sh))) : lo;
-        }
-      } else {
-        return tile_visibility(p.mask, rnode[r], rloc[r], P, kv_end, k0);
-      }
-      v |= t & range_bits(P - k0, kv_end - 1 - k0);
-    }
-    return v;
-  };
-
-  f32x4 o[RW][DU];
-  // fp32 row sums of P: each lane sums its own 16 keys of a row per tile;
-  // the 4 lanes of a row are added once, after the last tile
-  float l_lane[RW];
-  float m_run[RW], alpha[RW];
-#pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    m_run[r] = kNoMax;
-    l_lane[r] = 0.f;
-    alpha[r] = 1.f;
-#pragma unroll
-    for (int u = 0; u < DU; ++u) o[r][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  bool rescale = false;  // some row of the wave raised its running max: O *= alpha
 
   // ---- direct-to-LDS staging (dma_burst, tile_load_offsets): the first
   // NW/2 waves load K, the others V, one 16-key group (one page segment) of
@@ -609,6 +450,186 @@ void attn_bf16_kernel(Params p) {
       dma_burst<IPW>(src, voff, lds);
     }
   };
+
+  // Q fragments (B operand of S^T): lane (r16, q4) holds row r16 of its
+  // subtile, d = 32s + 8q4 .. +7. Subtiles st = wave + NW r hold rows
+  // row0 + 16 st ..; the first nv of them (a wave-uniform count) have a real
+  // row. Padding rows carry the request's first row's Q and are never
+  // stored, so the MFMAs below run unguarded. load_rows() issues these loads
+  // and the mask rows'; they stay in flight while the block's first K/V
+  // tiles are requested.
+  int nv = 0;
+#pragma unroll
+  for (int r = 0; r < RW; ++r) nv += (row0 + 16 * (wave + NW * r) < rows) ? 1 : 0;
+  bf16x8 qf[RW][DS];
+  int orow[RW], rnode[RW], rloc[RW];
+  bool row_ok[RW];
+  // per-row mask data kept in registers: ANCHOR (anchor_pos | branch_depth
+  // << 32 in m_w0), BITS with <= 2 words (the two words in m_w0, m_w1);
+  // wider BITS masks (the WIDE instantiation) are read per masked tile
+  const bool bits_in_regs = !WIDE && !anchor;
+  uint64_t m_w0[RW], m_w1[RW];
+  auto load_rows = [&]() {
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int row = row0 + 16 * (wave + NW * r) + r16;
+      row_ok[r] = row < rows;
+      const int i = row_ok[r] ? row / G : 0;
+      const int hl = row_ok[r] ? row % G : 0;
+      rloc[r] = i;
+      rnode[r] = n0 + i;
+      orow[r] = (n0 + i) * p.hq + g * G + hl;
+      // unconditional loads whose values are first used after the first tiles
+      // are requested: a padding row reads the request's first row (its scores
+      // are computed, never stored, and no other row depends on them; its mask
+      // is never consulted), and no select on the loaded values here, which
+      // would wait for them before the tile requests. With one mask word the
+      // second load reads the first again; bits past the last node are cut by
+      // the request's key range.
+      m_w0[r] = 0ull; m_w1[r] = 0ull;
+      if (anchor) {
+        m_w0[r] = (uint64_t)(uint32_t)p.mask.anchor_pos[rnode[r]] |
+                  ((uint64_t)(uint32_t)p.mask.branch_depth[rnode[r]] << 32);
+      } else if (bits_in_regs) {
+        m_w0[r] = p.mask.bits[(size_t)rnode[r] * p.mask.words];
+        m_w1[r] = p.mask.bits[(size_t)rnode[r] * p.mask.words + (p.mask.words - 1)];
+      }
+  #pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const uint4 u = *reinterpret_cast<const uint4*>(p.q + (size_t)orow[r] * D + 32 * s + 8 * q4);
+        qf[r][s] = __builtin_bit_cast(bf16x8, u);
+      }
+    }
+  };
+
+  // BITS form: no tile is skipped, so the block's first two tiles are known
+  // with the request's bounds. Each wave requests its share of them here,
+  // behind its Q and mask-row loads, with the page id read straight from
+  // the block table (the page list in LDS serves the later tiles).
+  static_assert(GPW == 1, "one page id per wave and tile");
+  auto table_page = [&](int k0, int (&pg)[GPW]) {
+    const int pos = min(k0 + 16 * gw, kv_end - 1);
+    pg[0] = clampi(row_tab[min(pos >> lp, p.max_pages - 1)], 0, p.num_pages - 1);
+  };
+  int pgn[GPW];
+  if (!anchor) {
+    load_rows();
+    if (ks < ke) { table_page(ks, pgn); issue(0, ks, pgn); }
+    if (ks + kTile < ke) { table_page(ks + kTile, pgn); issue(1, ks + kTile, pgn); }
+  }
+
+  if (anchor) {
+    const int node_lo = row0 / G;
+    int a_min = 0x7fffffff, a_max = -1, b_lo = 0x7fffffff;
+    for (int i = node_lo + tid; i <= node_hi; i += T) {
+      const int a = p.mask.anchor_pos[n0 + i], d = p.mask.branch_depth[n0 + i];
+      a_min = min(a_min, a);
+      a_max = max(a_max, a);
+      if (d > 0) b_lo = min(b_lo, i - d + 1);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      a_min = min(a_min, __shfl_xor(a_min, off, 64));
+      a_max = max(a_max, __shfl_xor(a_max, off, 64));
+      b_lo = min(b_lo, __shfl_xor(b_lo, off, 64));
+    }
+    if (lane == 0) { s_bounds[wave][0] = a_min; s_bounds[wave][1] = a_max; s_bounds[wave][2] = b_lo; }
+  }
+#pragma unroll
+  for (int j = 0; j < PPT; ++j) {
+    const int i = tid + j * T;
+    if (i < n_pg) s_pages[i] = clampi(pgv[j], 0, p.num_pages - 1);
+  }
+  // V of stage STAGES-1 is read (times P = 0) by the first M cluster
+  for (int c = tid; c < TILE_E / 8; c += T)
+    reinterpret_cast<uint4*>(&sV[STAGES - 1][0])[c] = uint4{0u, 0u, 0u, 0u};
+  // the page list, the partial bounds and the zeros are written; make them
+  // visible (this waits for the page table's and the bounds' loads, and in
+  // the BITS form for the first tiles and the Q and mask rows, which the
+  // first step needs anyway)
+  __builtin_amdgcn_s_waitcnt(W_ALL & ~0x0F00);
+  __syncthreads();
+  // Tile [k0, k0+64): skipped when it holds no prefix key and no tree key any
+  // row of the block can see (tree position j0 = k0 - P past every anchor,
+  // j0 + 63 before every branch start); unmasked when all its keys are
+  // visible to all.
+  // (unmasked: its keys lie before full_end = min(kv_end, P), or with the
+  // ANCHOR form min(kv_end, max(P, P + ap_min + 1)), set with the bounds)
+  int full_end = min(kv_end, P);
+  auto full_tile = [&](int k0) -> bool { return k0 + kTile <= full_end; };
+  // The skipped tiles of the split form one run of consecutive tile starts,
+  // [skip_from, skip_to) (set once the bounds are known; none by default).
+  int skip_from = 0x7fffffff, skip_to = 0x7fffffff;
+  auto next_tile = [&](int k0) {
+    const int k = k0 + kTile;
+    return k == skip_from ? skip_to : k;
+  };
+  if (anchor) {
+    int a_min = 0x7fffffff, a_max = -1, b_lo = 0x7fffffff;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      a_min = min(a_min, s_bounds[w][0]);
+      a_max = max(a_max, s_bounds[w][1]);
+      b_lo = min(b_lo, s_bounds[w][2]);
+    }
+    ap_min = a_min; ap_max = a_max; br_lo = b_lo;
+    full_end = (int)min((long long)kv_end, max((long long)P, (long long)P + ap_min + 1));
+    // tile starts ks + 64j skipped: from the first at or past
+    // max(P, P + ap_max + 1) up to the last at or before P + br_lo - 64
+    const long long lo = max((long long)P, (long long)P + ap_max + 1);
+    const long long hi = (long long)P + br_lo - kTile;
+    const long long f = ks + ((max(lo - ks, 0LL) + kTile - 1) / kTile) * kTile;
+    if (f <= hi && f < ke) {
+      skip_from = (int)f;
+      skip_to = (int)min((long long)ks + ((hi - ks) / kTile + 1) * kTile, (long long)ke);
+    }
+  }
+  // the block's first tiles (known before any tile is requested)
+  int c_cur = ks == skip_from ? skip_to : ks;
+  int c_prev = ke;  // tile m-1 (none yet)
+  int c_n1 = next_tile(c_cur), c_n2 = next_tile(c_n1);
+
+  // Visibility of keys [k0, k0 + 64) for this lane's row of subtile r.
+  auto row_visibility = [&](int r, int k0) -> uint64_t {
+    if (!row_ok[r]) return 0ull;
+    uint64_t v = range_bits(0, P - 1 - k0);
+    if (k0 + kTile > P && k0 < kv_end) {
+      const int j0 = k0 - P;  // > -64
+      uint64_t t;
+      if (anchor) {
+        const int ap = (int)(uint32_t)m_w0[r], bd = (int)(uint32_t)(m_w0[r] >> 32);
+        t = range_bits(-j0, ap - j0) | range_bits(rloc[r] - bd + 1 - j0, rloc[r] - j0);
+      } else if (!WIDE) {
+        if (j0 < 0) {
+          t = m_w0[r] << (-j0);
+        } else {
+          const int sh = j0 & 63;
+          const uint64_t lo = (j0 < 64) ? m_w0[r] : m_w1[r];
+          const uint64_t hi = (j0 < 64) ? m_w1[r] : 0ull;
+          t = sh ? ((lo >> sh) | (hi << (64 - sh))) : lo;
+        }
+      } else {
+        return tile_visibility(p.mask, rnode[r], rloc[r], P, kv_end, k0);
+      }
+      v |= t & range_bits(P - k0, kv_end - 1 - k0);
+    }
+    return v;
+  };
+
+  f32x4 o[RW][DU];
+  // fp32 row sums of P: each lane sums its own 16 keys of a row per tile;
+  // the 4 lanes of a row are added once, after the last tile
+  float l_lane[RW];
+  float m_run[RW], alpha[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    m_run[r] = kNoMax;
+    l_lane[r] = 0.f;
+    alpha[r] = 1.f;
+#pragma unroll
+    for (int u = 0; u < DU; ++u) o[r][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bool rescale = false;  // some row of the wave raised its running max: O *= alpha
 
   // ---- S^T = K Q^T of the tile in stage `buf`. Row 4c + i of subtile t of
   // S^T (the A-operand row fed from LDS) is key key_of(t, 4c + i) =
@@ -806,11 +827,13 @@ void attn_bf16_kernel(Params p) {
     probs(sc, pf);
   };
 
-  // The block's first two tiles, requested right after the Q and mask-row
-  // loads (the bounds that decide them are already known).
-  int pgn[GPW];
-  if (c_cur < ke) { pages_for(c_cur, pgn); issue(0, c_cur, pgn); }
-  if (c_n1 < ke) { pages_for(c_n1, pgn); issue(1, c_n1, pgn); }
+  // ANCHOR form: Q, the mask rows and the block's first two tiles once its
+  // bounds (which may skip tiles) are known.
+  if (anchor) {
+    load_rows();
+    if (c_cur < ke) { pages_for(c_cur, pgn); issue(0, c_cur, pgn); }
+    if (c_n1 < ke) { pages_for(c_n1, pgn); issue(1, c_n1, pgn); }
+  }
   // Solo blocks: the waves of group B hold no rows (at most 16*NW/2 rows),
   // so only group A reads the tiles and the stage of tile m-1 is free once
   // slot 2m ends. Tiles are then requested three ahead, in slot 2m+1, into
