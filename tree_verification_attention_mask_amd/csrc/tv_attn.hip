@@ -53,6 +53,7 @@ constexpr int kTile = 64;     // keys per tile
 constexpr int kMaxSplitPages = 4096;  // page ids one workgroup can stage (16-token pages: 64K keys)
 constexpr int kMaxLptBatch = 256;   // requests the in-kernel longest-first order handles
 constexpr float kLazyMax = 8.f;      // running-max slack before O is rescaled (log2 units)
+constexpr float kLazySum = 256.f;    // 2^kLazyMax
 // running max (log2 units) of a row before its first visible key: finite, so
 // that the probabilities' offset needs no select, and far below any score
 // (the first key raises it, with a rescale of the still-zero O and l by 0)
@@ -699,30 +700,25 @@ void attn_bf16_kernel(Params p) {
     }
     rescale = __builtin_amdgcn_ballot_w64(up_any) != 0;
   };
-  // ---- probabilities of a tile (bf16 B operand of the PV product)
-  auto probs = [&](f32x4 (&sacc)[RW][4], bf16x8 (&pf)[RW][2]) {
+  // ---- probabilities of a tile against the running max, 2^(s*scale - m),
+  // straight into the bf16 B operand of the PV product; `part` gets each
+  // lane's fp32 sum of its 16 values per row. The scores are left as they are.
+  auto probs = [&](const f32x4 (&sacc)[RW][4], float (&part)[RW], bf16x8 (&pf)[RW][2]) {
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
       const float m_use = m_run[r];
-      float part[4];
+      float pt[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sacc[r][t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r][t][i], p.scale_log2, -m_use));
-        part[t] = (sacc[r][t][0] + sacc[r][t][1]) + (sacc[r][t][2] + sacc[r][t][3]);
-      }
-      l_lane[r] += (part[0] + part[1]) + (part[2] + part[3]);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 f;
+        float e[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          f[i] = static_cast<__bf16>(sacc[r][2 * kk][i]);
-          f[4 + i] = static_cast<__bf16>(sacc[r][2 * kk + 1][i]);
+          e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r][t][i], p.scale_log2, -m_use));
+          pf[r][t >> 1][4 * (t & 1) + i] = static_cast<__bf16>(e[i]);
         }
-        pf[r][kk] = f;
+        pt[t] = (e[0] + e[1]) + (e[2] + e[3]);
       }
+      part[r] = (pt[0] + pt[1]) + (pt[2] + pt[3]);
     }
   };
   // ---- O^T += V^T P^T of the tile in stage `buf`. Element e of lane group
@@ -812,9 +808,30 @@ void attn_bf16_kernel(Params p) {
     __builtin_amdgcn_sched_group_barrier(0x008, RW * kAhead, 0);
     __builtin_amdgcn_s_setprio(0);
   };
+  // VALU cluster. Once the wave's rows hold a running max, the tile's
+  // probabilities are first taken against it as it stands: if no lane's sum
+  // of its 16 values of a row exceeds 2^kLazyMax, no value does, so no score
+  // rose more than kLazyMax above the max and the running max would not have
+  // moved -- the values are final, with no max of the tile taken at all.
+  // Otherwise (and for a wave's first tile) the max is taken from the scores,
+  // which the trial left in place, and raised with a rescale of O and l.
+  bool max_set = false;  // wave-uniform: the running maxima have been taken once
   auto cluster_v = [&](int k0) {
     if (nv == 0) return;
     if (!full_tile(k0)) apply_mask(k0, sc);
+    float part[RW];
+    if (max_set) {
+      probs(sc, part, pf);
+      bool big = false;
+#pragma unroll
+      for (int r = 0; r < RW; ++r) big = big || !(part[r] <= kLazySum);
+      if (__builtin_amdgcn_ballot_w64(big) == 0) {
+#pragma unroll
+        for (int r = 0; r < RW; ++r) l_lane[r] += part[r];
+        return;
+      }
+    }
+    max_set = true;
     row_update(sc);
     if (rescale) {
 #pragma unroll
@@ -824,7 +841,9 @@ void attn_bf16_kernel(Params p) {
         l_lane[r] *= alpha[r];
       }
     }
-    probs(sc, pf);
+    probs(sc, part, pf);
+#pragma unroll
+    for (int r = 0; r < RW; ++r) l_lane[r] += part[r];
   };
 
   // ANCHOR form: Q, the mask rows and the block's first two tiles once its
