@@ -1077,6 +1077,8 @@ void attn_bf16_short_kernel(Params p) {
   static_assert(IPW * RPI == 16 && IPW == VPG, "one 16-key group per wave and tile");
   __shared__ __attribute__((aligned(16))) __bf16 sK[kShortTiles][TILE_E];
   __shared__ __attribute__((aligned(16))) __bf16 sV[kShortTiles][TILE_E];
+  // each wave's Q fragments, fragment s of lane l at [wave][s][8 l]
+  __shared__ __attribute__((aligned(16))) __bf16 sQ[NW][DS][64 * 8];
 
   const int ng = p.batch * p.hkv * p.row_blocks;
   const int ng_pad = (ng + 7) & ~7;
@@ -1119,8 +1121,9 @@ void attn_bf16_short_kernel(Params p) {
   const int ke = min(min(ks + p.keys_per_split, kv_end), P + node_hi + 1);
   const int nt = ke > ks ? (ke - ks + kTile - 1) / kTile : 0;  // tiles in range, 0 .. kShortTiles
 
-  // ---- Q fragments and mask rows (padding rows read the request's first
-  // row), requested before the tiles so they land first
+  // ---- Q fragments, staged through LDS and requested before the tiles so
+  // they land first (their wait is counted below, as the tiles' are; padding
+  // rows read the request's first row)
   const int row = row0 + 16 * wave + r16;
   const bool row_ok = row < rows;
   const bool has_rows = row0 + 16 * wave < rows;  // wave-uniform
@@ -1128,19 +1131,9 @@ void attn_bf16_short_kernel(Params p) {
   const int rnode = n0 + li;
   const int orow = rnode * p.hq + g * G + (row_ok ? row % G : 0);
   const bool anchor = p.mask.kind == TV_MASK_ANCHOR;
-  uint64_t m_w0 = 0ull, m_w1 = 0ull;
-  if (anchor) {
-    m_w0 = (uint64_t)(uint32_t)p.mask.anchor_pos[rnode] |
-           ((uint64_t)(uint32_t)p.mask.branch_depth[rnode] << 32);
-  } else if (!WIDE) {
-    m_w0 = p.mask.bits[(size_t)rnode * p.mask.words];
-    m_w1 = p.mask.bits[(size_t)rnode * p.mask.words + (p.mask.words - 1)];
-  }
-  bf16x8 qf[DS];
 #pragma unroll
   for (int s = 0; s < DS; ++s)
-    qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
-                                           p.q + (size_t)orow * D + 32 * s + 8 * q4));
+    dma_single(p.q + (size_t)orow * D + 32 * s + 8 * q4, lds_u32(&sQ[wave][s][0]));
 
   // ---- all tiles of the split, straight into LDS (layouts as in the tile loop)
   uint32_t voff[IPW], lds0;
@@ -1157,10 +1150,30 @@ void attn_bf16_short_kernel(Params p) {
                       (uint32_t)(k_wave ? slot * D : slot) * sizeof(__bf16);
     dma_burst<IPW>(src, voff, lds0 + (uint32_t)(t * TILE_E * sizeof(__bf16)));
   }
-  // Q and mask rows are used from registers from here on
+  // this wave's Q fragments: its loads of them have landed once at most its
+  // tile loads are in flight (loads return in order); only this wave reads them
+  if (nt >= 4) wait_vmem<4 * IPW>();
+  else if (nt == 3) wait_vmem<3 * IPW>();
+  else if (nt == 2) wait_vmem<2 * IPW>();
+  else if (nt == 1) wait_vmem<IPW>();
+  else wait_vmem<0>();
+  asm volatile("" ::: "memory");
+  bf16x8 qf[DS];
 #pragma unroll
-  for (int s = 0; s < DS; ++s) asm volatile("" : "+v"(qf[s]));
-  asm volatile("" : "+v"(m_w0), "+v"(m_w1));
+  for (int s = 0; s < DS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(&sQ[wave][s][8 * lane]);
+  // mask rows, requested after the tiles: the first use of a plain load waits
+  // for every load in flight, and they are first used in a tile that reaches
+  // the tree keys (the last tiles of the request). Each form sets only the
+  // words it reads (a zero written into a register that the other form's load
+  // may still be filling would wait for every load in flight).
+  uint64_t m_w0, m_w1;
+  if (anchor) {
+    m_w0 = (uint64_t)(uint32_t)p.mask.anchor_pos[rnode] |
+           ((uint64_t)(uint32_t)p.mask.branch_depth[rnode] << 32);
+  } else if (!WIDE) {
+    m_w0 = p.mask.bits[(size_t)rnode * p.mask.words];
+    m_w1 = p.mask.bits[(size_t)rnode * p.mask.words + (p.mask.words - 1)];
+  }
 
   // visibility of keys [k0, k0 + 64) for this lane's row (as in the tile loop)
   auto row_visibility = [&](int k0) -> uint64_t {
@@ -1191,12 +1204,10 @@ void attn_bf16_short_kernel(Params p) {
   // ---- S^T = K Q^T of tile t (score rows permuted as in the tile loop: the
   // lane of row r16, column group q4 holds keys 32kk + 8q4 .. +7)
   auto key_of = [](int t, int m) { return 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3); };
-  f32x4 sc[kShortTiles][4];
-#pragma unroll
-  for (int t = 0; t < kShortTiles; ++t)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) sc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 sc[4];
   auto qk = [&](int t) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
 #pragma unroll
@@ -1204,85 +1215,83 @@ void attn_bf16_short_kernel(Params p) {
         const int krow = key_of(u, r16);
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
             &sK[t][krow * D + 8 * ((4 * s + q4) ^ kswz<D>(krow))]);
-        sc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sc[t][u], 0, 0, 0);
+        sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sc[u], 0, 0, 0);
       }
     }
   };
-  float m_row = -INFINITY, l_row = 0.f;
-  bf16x8 pf[kShortTiles][2];
-  // ---- mask, one row max, probabilities (bf16 B operand of PV), fp32 sums
-  auto softmax = [&]() {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < kShortTiles; ++t) {
-      const int k0 = ks + kTile * t;
-      const bool live = t < nt;
-      if (live && k0 + kTile > P) {
-        const uint64_t sh = row_visibility(k0) >> (8 * q4);
-        const uint32_t own = (uint32_t)(sh & 0xffu) | ((uint32_t)(sh >> 32) & 0xffu) << 8;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sc[t][u][i] = ((own >> (4 * u + i)) & 1u) ? sc[t][u][i] : -INFINITY;
-      }
-      if (live) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[t][u][i]);
-      }
-    }
-    m_row = row_max4(mx) * p.scale_log2;  // log2 units; -inf: no visible key here
-    const float m_use = (m_row == -INFINITY) ? 0.f : m_row;
-    float l_lane = 0.f;
-#pragma unroll
-    for (int t = 0; t < kShortTiles; ++t) {
-      float part[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sc[t][u][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][u][i], p.scale_log2, -m_use));
-        part[u] = (sc[t][u][0] + sc[t][u][1]) + (sc[t][u][2] + sc[t][u][3]);
-      }
-      if (t < nt) l_lane += (part[0] + part[1]) + (part[2] + part[3]);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f[i] = static_cast<__bf16>(sc[t][2 * kk][i]);
-          f[4 + i] = static_cast<__bf16>(sc[t][2 * kk + 1][i]);
-        }
-        pf[t][kk] = f;
-      }
-    }
-    l_row = row_sum4(l_lane);
-  };
-  // ---- O^T += V^T P^T
+  // ---- online softmax over the split's tiles, one tile at a time as it
+  // lands (running max in log2 units, raised lazily as in the tile loop)
+  float m_run = kNoMax, l_lane = 0.f;
+  bool max_set = false;  // wave-uniform: the running max has been taken once
+  bf16x8 pf[2];
   f32x4 o[DU];
 #pragma unroll
   for (int u = 0; u < DU; ++u) o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto pv = [&]() {
+  auto mask_tile = [&](int k0) {
+    const uint64_t sh = row_visibility(k0) >> (8 * q4);
+    const uint32_t own = (uint32_t)(sh & 0xffu) | ((uint32_t)(sh >> 32) & 0xffu) << 8;
 #pragma unroll
-    for (int t = 0; t < kShortTiles; ++t) {
-      if (t >= nt) continue;
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      for (int i = 0; i < 4; ++i) sc[u][i] = ((own >> (4 * u + i)) & 1u) ? sc[u][i] : -INFINITY;
+  };
+  // probabilities against the running max, straight into the bf16 B operand
+  // of the PV product; returns this lane's fp32 sum of its 16 values
+  auto probs = [&]() -> float {
+    float pt[4];
 #pragma unroll
-        for (int u = 0; u < DU; ++u) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
-              &sV[t][(2 * kk + (q4 >> 1)) * 16 * D + (16 * u + r16) * 16 + 8 * (q4 & 1)]);
-          o[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[t][kk], o[u], 0, 0, 0);
-        }
+    for (int u = 0; u < 4; ++u) {
+      float e[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][i], p.scale_log2, -m_run));
+        pf[u >> 1][4 * (u & 1) + i] = static_cast<__bf16>(e[i]);
+      }
+      pt[u] = (e[0] + e[1]) + (e[2] + e[3]);
+    }
+    return (pt[0] + pt[1]) + (pt[2] + pt[3]);
+  };
+  auto softmax_step = [&]() {
+    if (max_set) {
+      const float part = probs();
+      if (__builtin_amdgcn_ballot_w64(!(part <= kLazySum)) == 0) {
+        l_lane += part;
+        return;
+      }
+    }
+    max_set = true;
+    const float a0 = fmax3_raw(sc[0][0], sc[0][1], sc[0][2]);
+    const float a1 = fmax3_raw(sc[0][3], sc[1][0], sc[1][1]);
+    const float a2 = fmax3_raw(sc[1][2], sc[1][3], sc[2][0]);
+    const float a3 = fmax3_raw(sc[2][1], sc[2][2], sc[2][3]);
+    const float a4 = fmax3_raw(sc[3][0], sc[3][1], sc[3][2]);
+    const float mx = row_max4(fmax_raw(fmax3_raw(a0, a1, a2), fmax3_raw(a3, a4, sc[3][3]))) * p.scale_log2;
+    const bool up = mx > m_run + kLazyMax;
+    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+      const float alpha = up ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+#pragma unroll
+      for (int u = 0; u < DU; ++u) o[u] *= alpha;
+      l_lane *= alpha;
+      m_run = up ? mx : m_run;
+    }
+    l_lane += probs();
+  };
+  // ---- O^T += V^T P^T of tile t
+  auto pv = [&](int t) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int u = 0; u < DU; ++u) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
+            &sV[t][(2 * kk + (q4 >> 1)) * 16 * D + (16 * u + r16) * 16 + 8 * (q4 & 1)]);
+        o[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[kk], o[u], 0, 0, 0);
       }
     }
   };
 
   // ---- tiles land in order: wait for this wave's loads of tile t (counted
-  // vmcnt), then the barrier publishes every wave's part of it
-  const bool grp_b = wave >= NW / 2;
+  // vmcnt), then the barrier publishes every wave's part of it; each wave
+  // then takes the tile through S, the softmax step and O
   const bool tail = nt > 0 && ks + kTile * nt > kv_end;
 #pragma unroll
   for (int t = 0; t < kShortTiles; ++t) {
@@ -1296,7 +1305,7 @@ void attn_bf16_short_kernel(Params p) {
     if (t == nt - 1 && tail) {
       // V of the positions past the request's last key (cache slots the
       // caller never wrote) must be finite zeros: P = 0 there. Published by
-      // the barrier below, before any PV.
+      // a second barrier, before the PV product of this tile.
       const int lim = kv_end - (ks + kTile * t);
       for (int c = tid; c < TILE_E / 8; c += T) {
         const int e = 8 * c;
@@ -1309,25 +1318,18 @@ void attn_bf16_short_kernel(Params p) {
         *ch = v;
       }
       __builtin_amdgcn_s_waitcnt(W_ALL & ~0x0F00);
+      __builtin_amdgcn_s_barrier();
     }
-    if (!grp_b && has_rows) qk(t);
-  }
-  if (nt == 0) wait_vmem<0>();  // Q and mask rows
-  __builtin_amdgcn_s_barrier();
-  if (has_rows) {
-    if (grp_b) {
-#pragma unroll
-      for (int t = 0; t < kShortTiles; ++t)
-        if (t < nt) qk(t);
-    } else {
-      softmax();
+    if (has_rows) {
+      const int k0 = ks + kTile * t;
+      qk(t);
+      if (k0 + kTile > P) mask_tile(k0);
+      softmax_step();
+      pv(t);
     }
   }
-  __builtin_amdgcn_s_barrier();
-  if (has_rows) {
-    if (grp_b) softmax();
-    pv();
-  }
+  const float l_row = row_sum4(l_lane);
+  const float m_row = l_row > 0.f ? m_run : -INFINITY;
 
   // ---- epilogue: lane (r16, q4) holds O[row r16][16u + 4q4 + i]
   const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
