@@ -664,11 +664,17 @@ void attn_bf16_kernel(Params p) {
       // this lane's 16 keys key_of(t, 4q4 + i) as bits 4t + i of `own`
       const uint64_t sh = row_visibility(r, k0) >> (8 * q4);
       const uint32_t own = (uint32_t)(sh & 0xffu) | ((uint32_t)(sh >> 32) & 0xffu) << 8;
+      // bit 4t + i of `own` spread over the score's 32 bits (one bit-field
+      // extract), then the score or -inf by that mask (one bit-field insert)
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sacc[r][t][i] = ((own >> (4 * t + i)) & 1u) ? sacc[r][t][i] : -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t keep = (uint32_t)((int32_t)(own << (31 - (4 * t + i))) >> 31);
+          const float sv = sacc[r][t][i];  // (a bit cast of a vector element
+          const uint32_t sb = __builtin_bit_cast(uint32_t, sv);  // itself reads element 0)
+          sacc[r][t][i] = __builtin_bit_cast(float, (sb & keep) | (0xff800000u & ~keep));
+        }
     }
   };
   // ---- running max from a tile's (masked) scores. The max is raised only
@@ -822,10 +828,10 @@ void attn_bf16_kernel(Params p) {
     float part[RW];
     if (max_set) {
       probs(sc, part, pf);
-      bool big = false;
+      uint64_t big = 0;  // lanes with a sum past the slack (or NaN), one compare each
 #pragma unroll
-      for (int r = 0; r < RW; ++r) big = big || !(part[r] <= kLazySum);
-      if (__builtin_amdgcn_ballot_w64(big) == 0) {
+      for (int r = 0; r < RW; ++r) big |= __builtin_amdgcn_ballot_w64(!(part[r] <= kLazySum));
+      if (big == 0) {
 #pragma unroll
         for (int r = 0; r < RW; ++r) l_lane[r] += part[r];
         return;
