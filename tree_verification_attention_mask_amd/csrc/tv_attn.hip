@@ -1373,19 +1373,20 @@ void attn_bf16_short_kernel(Params p) {
 
 // Merge of split partials: m = max m_s, l = sum 2^(m_s - m) l_s,
 // o = sum 2^(m_s - m) l_s o_s / l (o_s the split's own average, bf16),
-// lse = (m + log2 l) ln 2. One row per D/4
-// lanes; the partials of 16 splits are loaded at once (one round trip), and
-// longer split lists are folded in chunks with the same online rescaling.
+// lse = (m + log2 l) ln 2. One row per D/4 lanes; the partials of CH splits
+// (CH >= splits when splits <= 16) are loaded at once, unconditionally (a
+// chunk's positions past the last split reload the last split and count as
+// empty), so every load of a chunk is in flight together: one round trip.
+// Longer split lists are folded in chunks with the same online rescaling.
 // Every (split, row) pair holds a partial or an empty marker (m = -inf),
 // whose o is never read into the sums.
-template <int D, typename OutT>
+template <int D, int CH, typename OutT>
 __global__ __launch_bounds__(256) void combine_kernel(const __bf16* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       int64_t R_tot, int32_t splits,
                                                       OutT* __restrict__ out, float* __restrict__ lse) {
   constexpr int LPR = D / 4;               // lanes per row
   constexpr int RPB = 256 / LPR;           // rows per block
-  constexpr int CH = 16;                   // splits per chunk
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   const int sub = threadIdx.x % LPR;
   if (row >= R_tot) return;
@@ -1396,15 +1397,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const __bf16* __restrict__
     bf16x4 os[CH];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int64_t pr = (int64_t)(s0 + j) * R_tot + row;
-      const bool ok = s0 + j < splits;
-      ml[j] = ok ? *reinterpret_cast<const float2*>(part_ml + pr * 2) : float2{-INFINITY, 0.f};
-      os[j] = ok ? *reinterpret_cast<const bf16x4*>(part_o + pr * D + 4 * sub) : bf16x4{};
+      const int64_t pr = (int64_t)min(s0 + j, splits - 1) * R_tot + row;
+      ml[j] = *reinterpret_cast<const float2*>(part_ml + pr * 2);
+      os[j] = *reinterpret_cast<const bf16x4*>(part_o + pr * D + 4 * sub);
     }
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+      if (s0 + j >= splits) ml[j].x = -INFINITY;
+    // (no early exit for an all-empty chunk: a branch on the maxima would
+    // hold the other loads back until they are known, a second round trip)
     float mc = m;
 #pragma unroll
     for (int j = 0; j < CH; ++j) mc = fmaxf(mc, ml[j].x);
-    if (mc == -INFINITY) continue;
     const float a = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mc);
     l *= a;
     acc *= a;
@@ -1413,7 +1417,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const __bf16* __restrict__
       const bool live = ml[j].x != -INFINITY;
       const float w = live ? __builtin_amdgcn_exp2f(ml[j].x - mc) : 0.f;
       const float wl = w * ml[j].y;
-      l += wl;
+      l += live ? wl : 0.f;
       f32x4 o4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) o4[i] = static_cast<float>(os[j][i]);
@@ -1605,6 +1609,26 @@ AttnPlan plan_attn(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_
   }
   return pl;
 }
+// the merge with the smallest chunk that holds every split (16 at most)
+template <int D>
+hipError_t launch_combine(const Params& p, int splits, int64_t rtot, float* lse, hipStream_t stream) {
+  constexpr int rpb = 256 / (D / 4);
+  const int cgrid = (int)((rtot + rpb - 1) / rpb);
+  if (splits <= 2)
+    hipLaunchKernelGGL((combine_kernel<D, 2, __bf16>), dim3(cgrid), dim3(256), 0, stream, p.part_o,
+                       p.part_ml, rtot, splits, p.out, lse);
+  else if (splits <= 4)
+    hipLaunchKernelGGL((combine_kernel<D, 4, __bf16>), dim3(cgrid), dim3(256), 0, stream, p.part_o,
+                       p.part_ml, rtot, splits, p.out, lse);
+  else if (splits <= 8)
+    hipLaunchKernelGGL((combine_kernel<D, 8, __bf16>), dim3(cgrid), dim3(256), 0, stream, p.part_o,
+                       p.part_ml, rtot, splits, p.out, lse);
+  else
+    hipLaunchKernelGGL((combine_kernel<D, 16, __bf16>), dim3(cgrid), dim3(256), 0, stream, p.part_o,
+                       p.part_ml, rtot, splits, p.out, lse);
+  return hipGetLastError();
+}
+
 
 hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream) {
   const int G = a.hq / a.hkv;
@@ -1667,15 +1691,8 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& plan, hipStream_t stre
   hipError_t e = (a.head_dim == 64) ? dispatch_bf16<64>(p, plan, grid, stream)
                                     : dispatch_bf16<128>(p, plan, grid, stream);
   if (e != hipSuccess || plan.splits == 1) return e;
-  const int lpr = a.head_dim / 4, rpb = 256 / lpr;
-  const int cgrid = (int)((rtot + rpb - 1) / rpb);
-  if (a.head_dim == 64)
-    hipLaunchKernelGGL((combine_kernel<64, __bf16>), dim3(cgrid), dim3(256), 0, stream, p.part_o,
-                       p.part_ml, (int64_t)rtot, plan.splits, p.out, a.lse);
-  else
-    hipLaunchKernelGGL((combine_kernel<128, __bf16>), dim3(cgrid), dim3(256), 0, stream, p.part_o,
-                       p.part_ml, (int64_t)rtot, plan.splits, p.out, a.lse);
-  return hipGetLastError();
+  return (a.head_dim == 64) ? launch_combine<64>(p, plan.splits, rtot, a.lse, stream)
+                            : launch_combine<128>(p, plan.splits, rtot, a.lse, stream);
 }
 
 }  // namespace tv
