@@ -1337,38 +1337,65 @@ void attn_bf16_short_kernel(Params p) {
   const float l_row = row_sum4(l_lane);
   const float m_row = l_row > 0.f ? m_run : -INFINITY;
 
-  // ---- epilogue: lane (r16, q4) holds O[row r16][16u + 4q4 + i]
+  // ---- epilogue: lane (r16, q4) holds O[row r16][16u + 4q4 + i]. The
+  // wave's 16 rows go through its own Q stage in LDS (no longer read; 16-byte
+  // chunks XOR-swizzled by row), so that each store instruction writes whole
+  // rows, 16 bytes a lane, instead of 8-byte pieces of 16 rows.
+  constexpr int CPR16 = D / 8;         // 16-byte chunks per row
+  constexpr int RPS = 64 / CPR16;      // rows per store instruction
+  auto swz = [](int rr) { return rr & (CPR16 - 1); };
   const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
-  if (p.splits == 1) {
-    if (!row_ok) return;
+  char* ep = reinterpret_cast<char*>(&sQ[wave][0][0]);
+  if (p.splits == 1 || nt > 0) {
 #pragma unroll
     for (int u = 0; u < DU; ++u) {
       bf16x4 h;
 #pragma unroll
       for (int i = 0; i < 4; ++i) h[i] = static_cast<__bf16>(o[u][i] * inv);
-      *reinterpret_cast<bf16x4*>(p.out + (size_t)orow * D + 16 * u + 4 * q4) = h;
+      const int c = 2 * u + (q4 >> 1);
+      *reinterpret_cast<bf16x4*>(ep + r16 * (2 * D) + ((c ^ swz(r16)) << 4) + 8 * (q4 & 1)) = h;
     }
-    if (p.lse && q4 == 0)
-      p.lse[orow] = l_row > 0.f ? (m_row + log2f(l_row)) * kLn2 : -INFINITY;
+  }
+  const size_t obase = p.splits == 1 ? 0 : (size_t)split * p.total_nodes * p.hq;
+  // row rr of the wave's 16 and the 16-byte chunk c of it that this lane
+  // stores in store instruction m; false past the request's rows
+  auto chunk = [&](int m, size_t& off, bf16x8& v) -> bool {
+    const int rr = RPS * m + lane / CPR16, c = lane % CPR16;
+    const int rw = row0 + 16 * wave + rr;
+    off = (obase + (size_t)(n0 + rw / G) * p.hq + g * G + rw % G) * D + 8 * c;
+    v = *reinterpret_cast<const bf16x8*>(ep + rr * (2 * D) + ((c ^ swz(rr)) << 4));
+    return rw < rows;
+  };
+  if (p.splits == 1) {
+#pragma unroll
+    for (int m = 0; m < 16 / RPS; ++m) {
+      size_t off;
+      bf16x8 v;
+      if (chunk(m, off, v)) *reinterpret_cast<bf16x8*>(p.out + off) = v;
+    }
+  } else if (nt > 0) {
+    // partials: nontemporal (less dirty L2 to write back when the kernel ends)
+#pragma unroll
+    for (int m = 0; m < 16 / RPS; ++m) {
+      size_t off;
+      bf16x8 v;
+      if (chunk(m, off, v)) __builtin_nontemporal_store(v, reinterpret_cast<bf16x8*>(p.part_o + off));
+    }
+    // (keeps the compiler from sinking the last store of each loop into one
+    // shared store, which drops the nontemporal hint)
+    asm volatile("; partial rows stored" ::: "memory");
+  }
+  if (!row_ok || q4 != 0) return;
+  if (p.splits == 1) {
+    if (p.lse) p.lse[orow] = l_row > 0.f ? (m_row + log2f(l_row)) * kLn2 : -INFINITY;
     return;
   }
   // partials for the merge kernel, [split][total_nodes * hq] rows; a split
   // with no key for this block stores only its empty marker (m = -inf,
   // l = 0: the merge never reads that split's o)
-  if (!row_ok) return;
-  const size_t prow = (size_t)split * p.total_nodes * p.hq + orow;
-  if (nt > 0)
-#pragma unroll
-  for (int u = 0; u < DU; ++u) {
-    bf16x4 h;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) h[i] = static_cast<__bf16>(o[u][i] * inv);
-    __builtin_nontemporal_store(h, reinterpret_cast<bf16x4*>(p.part_o + prow * D + 16 * u + 4 * q4));
-  }
-  if (q4 == 0) {
-    __builtin_nontemporal_store(m_row, p.part_ml + prow * 2);
-    __builtin_nontemporal_store(l_row, p.part_ml + prow * 2 + 1);
-  }
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  __builtin_nontemporal_store(f32x2{m_row, l_row},
+                              reinterpret_cast<f32x2*>(p.part_ml + (obase + orow) * 2));
 }
 
 // Merge of split partials: m = max m_s, l = sum 2^(m_s - m) l_s,
