@@ -90,6 +90,20 @@ def test_attention_plan_follows_the_compute_unit_count(cus, shape):
                                                   binding.torch.bfloat16) == pl["workspace_bytes"]
 
 
+def test_merge_chunk_shapes_reach_every_chunk_size():
+    """The GPU test of the merge's chunk sizes (2, 4, 8 and 16 split
+    positions loaded at once) uses shapes whose 256-CU plans reach each size."""
+    import test_gpu_2_attn as t2
+    seen = {}
+    for batch, hq, hkv, prefix, nodes in t2._MERGE_CHUNK_SHAPES:
+        pl = tv.verify_attn_plan(batch, batch * nodes, nodes, prefix, hq, hkv, 128,
+                                 binding.torch.bfloat16, 256)
+        s = pl["splits"]
+        seen[2 if s <= 2 else 4 if s <= 4 else 8 if s <= 8 else 16] = s
+    assert set(seen) == {2, 4, 8, 16}, seen
+    assert all(s not in (2, 4, 8, 16) for s in list(seen.values())[1:]), seen  # unused positions
+
+
 def test_attention_plan_splits_grow_with_the_compute_units():
     s = [tv.verify_attn_plan(1, 60, 60, 2048, 32, 8, 128, binding.torch.bfloat16, c)["splits"]
          for c in (80, 256, 304)]

@@ -391,3 +391,35 @@ def test_split_merge_reads_this_calls_partials(shape):
         ref, rlse = oracle_attn(w)
         print(shape, call, assert_attn_close(out, ref, "bf16", lse, rlse,
                                               what="%s call %d" % (shape, call)))
+
+
+# (batch, q heads, kv heads, prefix, tree nodes): on a 256-CU GPU these plan
+# 2 splits of the tile loop, 3, 5 and 12 one-shot splits -- merge chunks of
+# 2, 4, 8 and 16 positions, the last three with unused positions at the end
+_MERGE_CHUNK_SHAPES = [(16, 16, 8, 1230, 9), (10, 16, 8, 600, 12), (5, 16, 8, 900, 10),
+                       (2, 16, 8, 1500, 14)]
+
+
+@pytest.mark.parametrize("shape", _MERGE_CHUNK_SHAPES)
+def test_split_merge_chunk_sizes(shape):
+    """The merge loads a chunk of 2, 4, 8 or 16 split positions at once, the
+    positions past the last split reloading it and counting as empty: every
+    chunk size, with a poisoned workspace (0xFF bytes: NaN as bf16 and fp32)
+    before the call, against the oracle over every output."""
+    batch, hq, hkv, prefix, nodes = shape
+    rng = np.random.default_rng(batch * 1000 + prefix)
+    trees = [W.random_tree(rng, nodes) for _ in range(batch)]
+    w = W.build_workload("merge-chunks", trees, [prefix] * batch, hq, hkv, 128, "bf16", rng,
+                         permute_pages=True, tokens=False)
+    pl = tv.verify_attn_plan(w.batch, w.total_nodes, w.max_nodes, w.max_prefix_len,
+                             w.num_q_heads, w.num_kv_heads, w.head_dim, torch.bfloat16)
+    print(shape, pl, flush=True)
+    assert pl["splits"] > 1
+    d = Dev(w)
+    ws = torch.empty(pl["workspace_bytes"], dtype=torch.uint8, device="cuda")
+    ws.fill_(255)
+    out, lse = d.attn(workspace=ws)
+    torch.cuda.synchronize()
+    ref, rlse = oracle_attn(w)
+    print(shape, assert_attn_close(out, ref, "bf16", lse, rlse, what="merge chunks %s" % (shape,)))
+

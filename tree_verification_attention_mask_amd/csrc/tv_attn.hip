@@ -1621,8 +1621,7 @@ AttnPlan plan_attn(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_
   const long tps = (tiles + splits - 1) / splits;
   pl.keys_per_split = (int)(tps * kTile);
   pl.splits = (int)((tiles + tps - 1) / tps);
-  // splits of a few tiles take the one-shot kernel (128-row blocks), which
-  // also merges them itself when there are not too many
+  // splits of a few tiles take the one-shot kernel (128-row blocks)
   pl.short_splits = (pl.rw == 1 && tps <= kShortTiles) ? 1 : 0;
   if (pl.splits > 1) {
     const size_t rtot = (size_t)total_nodes * hq;
