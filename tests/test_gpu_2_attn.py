@@ -423,3 +423,27 @@ def test_split_merge_chunk_sizes(shape):
     ref, rlse = oracle_attn(w)
     print(shape, assert_attn_close(out, ref, "bf16", lse, rlse, what="merge chunks %s" % (shape,)))
 
+
+
+def test_split_merge_256_row_blocks_whole_output():
+    """Key splits of the 256-row tile loop merged over a poisoned workspace
+    (0xFF bytes): 4 requests of a 64-node tree over 3000 keys, 64 q / 8 kv
+    heads (4 splits, 16,384 rows), every output against the oracle."""
+    rng = np.random.default_rng(77)
+    trees = [W.random_tree(rng, 64) for _ in range(4)]
+    w = W.build_workload("merge-256", trees, [3000] * 4, 64, 8, 128, "bf16", rng,
+                         permute_pages=True, tokens=False)
+    pl = tv.verify_attn_plan(w.batch, w.total_nodes, w.max_nodes, w.max_prefix_len,
+                             w.num_q_heads, w.num_kv_heads, w.head_dim, torch.bfloat16)
+    print("merge-256", pl, flush=True)
+    assert pl["splits"] > 1 and pl["rows_per_block"] == 256
+    d = Dev(w)
+    ws = torch.empty(pl["workspace_bytes"], dtype=torch.uint8, device="cuda")
+    ws.fill_(255)
+    out, lse = d.attn(workspace=ws)
+    torch.cuda.synchronize()
+    ref, rlse = oracle_attn_threaded(w)
+    rows = all_rows(w)
+    got = out[rows[:, 0], rows[:, 1]].float().cpu().numpy()
+    gl = lse[rows[:, 0], rows[:, 1]].cpu().numpy()
+    print("merge-256", assert_attn_close(got, ref, "bf16", gl, rlse, what="merge-256"))
