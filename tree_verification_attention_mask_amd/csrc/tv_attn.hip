@@ -347,15 +347,30 @@ void attn_bf16_kernel(Params p) {
   const int n_pg = max(1, min(((ks + p.keys_per_split + kTile - 1) >> lp) - pg_lo + 1, kMaxSplitPages));
   int pgv[PPT];
   const int32_t* row_tab = p.block_table + (size_t)b * p.max_pages;
+  // page ids of this wave's 16-key group of the block's first two tiles,
+  // straight from the block table and loaded first, with the request's
+  // bounds: the tiles go out as soon as those are known (an entry past the
+  // request's pages is clamped into the pool; its keys are masked and its
+  // V zeroed)
+  int pgf[2];
+#pragma unroll
+  for (int t2 = 0; t2 < 2; ++t2)
+    pgf[t2] = row_tab[min((ks + kTile * t2 + 16 * ((wave < NW / 2 ? wave : wave - NW / 2) * GPW)) >> lp,
+                          p.max_pages - 1)];
 #pragma unroll
   for (int j = 0; j < PPT; ++j) {
     const int i = tid + j * T;
     pgv[j] = (i < n_pg) ? row_tab[min(pg_lo + i, p.max_pages - 1)] : 0;
   }
 
-  const int n0 = clampi(p.cu_nodes[b], 0, p.total_nodes);
-  const int n = clampi(p.cu_nodes[b + 1], n0, p.total_nodes) - n0;
-  const int P = max(p.prefix_len[b], 0);
+  // the request's bounds and the first page ids in one round trip: held in
+  // registers here, so that no load is moved past the early exits below
+  // (where it would start a second round trip)
+  int cu_lo = p.cu_nodes[b], cu_hi = p.cu_nodes[b + 1], p_len = p.prefix_len[b];
+  asm volatile("" : "+s"(cu_lo), "+s"(cu_hi), "+s"(p_len), "+s"(pgf[0]), "+s"(pgf[1]));
+  const int n0 = clampi(cu_lo, 0, p.total_nodes);
+  const int n = clampi(cu_hi, n0, p.total_nodes) - n0;
+  const int P = max(p_len, 0);
   const int G = p.group;
   const int rows = n * G;
   const int row0 = rb * MBLK;
@@ -382,12 +397,10 @@ void attn_bf16_kernel(Params p) {
 
   // ANCHOR form: block-wide bounds to skip tree tiles no row can see and to
   // treat tiles every row sees in full as unmasked: the min and max anchor
-  // and the lowest branch start over the block's nodes. Their loads go out
-  // here, behind only the page-table loads that the barrier below waits for
-  // anyway and ahead of every Q, mask-row and tile load (loads return in
-  // order: a bound loaded after the tile requests would wait for the tiles).
-  // Each wave folds its nodes with a butterfly; the barrier publishes the
-  // waves' partial bounds.
+  // and the lowest branch start over the block's nodes (their loads go out
+  // below, ahead of the Q, mask-row and first tile loads). Each wave folds
+  // its nodes with a butterfly; the barrier publishes the waves' partial
+  // bounds.
   int ap_min = -1, ap_max = 0x7fffffff, br_lo = 0x7fffffff;
   const bool anchor = p.mask.kind == TV_MASK_ANCHOR;
 
@@ -465,11 +478,14 @@ void attn_bf16_kernel(Params p) {
   bf16x8 qf[RW][DS];
   int orow[RW], rnode[RW], rloc[RW];
   bool row_ok[RW];
-  // per-row mask data kept in registers: ANCHOR (anchor_pos | branch_depth
-  // << 32 in m_w0), BITS with <= 2 words (the two words in m_w0, m_w1);
-  // wider BITS masks (the WIDE instantiation) are read per masked tile
+  // per-row mask data kept in registers: ANCHOR (anchor_pos and
+  // branch_depth in m_ap, m_bd), BITS with <= 2 words (the two words in
+  // m_w0, m_w1); wider BITS masks (the WIDE instantiation) are read per
+  // masked tile. (Separate registers per form: one 64-bit value built from
+  // either form's loads needed copies that waited for every load in flight.)
   const bool bits_in_regs = !WIDE && !anchor;
   uint64_t m_w0[RW], m_w1[RW];
+  uint32_t m_ap[RW], m_bd[RW];
   auto load_rows = [&]() {
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
@@ -487,10 +503,12 @@ void attn_bf16_kernel(Params p) {
       // would wait for them before the tile requests. With one mask word the
       // second load reads the first again; bits past the last node are cut by
       // the request's key range.
-      m_w0[r] = 0ull; m_w1[r] = 0ull;
+      // (each form sets only its own registers: a constant written into a
+      // register that the other form's load may still be filling would wait
+      // for every load in flight)
       if (anchor) {
-        m_w0[r] = (uint64_t)(uint32_t)p.mask.anchor_pos[rnode[r]] |
-                  ((uint64_t)(uint32_t)p.mask.branch_depth[rnode[r]] << 32);
+        m_ap[r] = (uint32_t)p.mask.anchor_pos[rnode[r]];
+        m_bd[r] = (uint32_t)p.mask.branch_depth[rnode[r]];
       } else if (bits_in_regs) {
         m_w0[r] = p.mask.bits[(size_t)rnode[r] * p.mask.words];
         m_w1[r] = p.mask.bits[(size_t)rnode[r] * p.mask.words + (p.mask.words - 1)];
@@ -503,30 +521,36 @@ void attn_bf16_kernel(Params p) {
     }
   };
 
-  // BITS form: no tile is skipped, so the block's first two tiles are known
-  // with the request's bounds. Each wave requests its share of them here,
-  // behind its Q and mask-row loads, with the page id read straight from
-  // the block table (the page list in LDS serves the later tiles).
+  // The block's first two tiles go out with its Q and mask rows, as soon as
+  // the request's bounds are known, with the page ids loaded beside those.
+  // BITS form: no tile is skipped, so they are tiles ks and ks + 64. ANCHOR
+  // form: the same two are requested before the anchor bounds tell whether
+  // they are skipped (tile ks is whenever a split starts inside the run no
+  // row of the block sees); the anchor bounds' loads go out first, and a
+  // wrong guess is requested again below once the bounds are known (its
+  // stale loads land first: one wave's loads return in order). The page
+  // list in LDS serves the later tiles.
   static_assert(GPW == 1, "one page id per wave and tile");
-  auto table_page = [&](int k0, int (&pg)[GPW]) {
-    const int pos = min(k0 + 16 * gw, kv_end - 1);
-    pg[0] = clampi(row_tab[min(pos >> lp, p.max_pages - 1)], 0, p.num_pages - 1);
-  };
   int pgn[GPW];
-  if (!anchor) {
-    load_rows();
-    if (ks < ke) { table_page(ks, pgn); issue(0, ks, pgn); }
-    if (ks + kTile < ke) { table_page(ks + kTile, pgn); issue(1, ks + kTile, pgn); }
+  // ANCHOR: the block's nodes (at most 256, one per thread) for its bounds
+  const int node_lo = row0 / G;
+  const int a_node = min(node_lo + tid, node_hi);
+  int a_ld = 0, d_ld = 0;
+  if (anchor) {
+    a_ld = p.mask.anchor_pos[n0 + a_node];
+    d_ld = p.mask.branch_depth[n0 + a_node];
   }
+  load_rows();
+  if (ks < ke) { pgn[0] = clampi(pgf[0], 0, p.num_pages - 1); issue(0, ks, pgn); }
+  if (ks + kTile < ke) { pgn[0] = clampi(pgf[1], 0, p.num_pages - 1); issue(1, ks + kTile, pgn); }
 
   if (anchor) {
-    const int node_lo = row0 / G;
+    static_assert(MBLK <= T, "one node of the block per thread");
     int a_min = 0x7fffffff, a_max = -1, b_lo = 0x7fffffff;
-    for (int i = node_lo + tid; i <= node_hi; i += T) {
-      const int a = p.mask.anchor_pos[n0 + i], d = p.mask.branch_depth[n0 + i];
-      a_min = min(a_min, a);
-      a_max = max(a_max, a);
-      if (d > 0) b_lo = min(b_lo, i - d + 1);
+    if (node_lo + tid <= node_hi) {
+      a_min = a_ld;
+      a_max = a_ld;
+      if (d_ld > 0) b_lo = a_node - d_ld + 1;
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
@@ -598,7 +622,7 @@ void attn_bf16_kernel(Params p) {
       const int j0 = k0 - P;  // > -64
       uint64_t t;
       if (anchor) {
-        const int ap = (int)(uint32_t)m_w0[r], bd = (int)(uint32_t)(m_w0[r] >> 32);
+        const int ap = (int)m_ap[r], bd = (int)m_bd[r];
         t = range_bits(-j0, ap - j0) | range_bits(rloc[r] - bd + 1 - j0, rloc[r] - j0);
       } else if (!WIDE) {
         if (j0 < 0) {
@@ -852,12 +876,10 @@ void attn_bf16_kernel(Params p) {
     for (int r = 0; r < RW; ++r) l_lane[r] += part[r];
   };
 
-  // ANCHOR form: Q, the mask rows and the block's first two tiles once its
-  // bounds (which may skip tiles) are known.
+  // ANCHOR form: the first two tiles again where the bounds skip the guess
   if (anchor) {
-    load_rows();
-    if (c_cur < ke) { pages_for(c_cur, pgn); issue(0, c_cur, pgn); }
-    if (c_n1 < ke) { pages_for(c_n1, pgn); issue(1, c_n1, pgn); }
+    if (c_cur < ke && c_cur != ks) { pages_for(c_cur, pgn); issue(0, c_cur, pgn); }
+    if (c_n1 < ke && c_n1 != ks + kTile) { pages_for(c_n1, pgn); issue(1, c_n1, pgn); }
   }
   // Solo blocks: the waves of group B hold no rows (at most 16*NW/2 rows),
   // so only group A reads the tiles and the stage of tile m-1 is free once
@@ -869,7 +891,7 @@ void attn_bf16_kernel(Params p) {
   // waits for them, and for the tiles requested above)
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
-    asm volatile("" : "+v"(m_w0[r]), "+v"(m_w1[r]));
+    asm volatile("" : "+v"(m_w0[r]), "+v"(m_w1[r]), "+v"(m_ap[r]), "+v"(m_bd[r]));
 #pragma unroll
     for (int s = 0; s < DS; ++s) asm volatile("" : "+v"(qf[r][s]));
   }
