@@ -447,3 +447,33 @@ def test_split_merge_256_row_blocks_whole_output():
     got = out[rows[:, 0], rows[:, 1]].float().cpu().numpy()
     gl = lse[rows[:, 0], rows[:, 1]].cpu().numpy()
     print("merge-256", assert_attn_close(got, ref, "bf16", gl, rlse, what="merge-256"))
+
+
+def test_anchor_form_splits_starting_in_skipped_tiles_whole_output():
+    """ANCHOR form with key splits (the tile loop, 256-row blocks): the block
+    requests its split's first two tiles before its anchor bounds are known
+    and requests them again where the bounds skip them. A 3072-token trunk
+    with 8 branches of 16 hanging off anchors below 1024, 2 q / 1 kv head:
+    10 splits of 320 keys, so for the branch nodes' block every split from
+    key 1280 on starts inside the run of trunk tiles no row of the block
+    sees. Every output against the oracle, poisoned workspace."""
+    rng = np.random.default_rng(5)
+    anchors = np.sort(rng.choice(np.arange(64, 1024), size=8, replace=False))
+    par = W.trunk_branch_tree(3072, anchors.tolist(), 16)
+    w = W.build_workload("anchor-splits", [par], [0], 2, 1, 128, "bf16", rng, tokens=False,
+                         mask_kind="anchor")
+    pl = tv.verify_attn_plan(w.batch, w.total_nodes, w.max_nodes, w.max_prefix_len,
+                             w.num_q_heads, w.num_kv_heads, w.head_dim, torch.bfloat16)
+    print("anchor-splits", anchors.tolist(), pl, flush=True)
+    assert pl["splits"] > 2 and pl["rows_per_block"] == 256
+    assert pl["keys_per_split"] * (pl["splits"] - 1) > int(anchors.max()) + 64
+    d = Dev(w)
+    ws = torch.empty(pl["workspace_bytes"], dtype=torch.uint8, device="cuda")
+    ws.fill_(255)
+    out, lse = d.attn(mask=d.mask("anchor"), workspace=ws)
+    torch.cuda.synchronize()
+    ref, rlse = oracle_attn_threaded(w)
+    rows = all_rows(w)
+    got = out[rows[:, 0], rows[:, 1]].float().cpu().numpy()
+    gl = lse[rows[:, 0], rows[:, 1]].cpu().numpy()
+    print("anchor-splits", assert_attn_close(got, ref, "bf16", gl, rlse, what="anchor-splits"))
