@@ -1068,11 +1068,10 @@ void attn_bf16_kernel(Params p) {
 // many workgroups, e.g. a 60-node tree behind a 2048-key prefix), the tile
 // loop's per-tile barriers and pipeline fill cost more than its arithmetic.
 // Here a workgroup of 8 waves (16 rows each, 128 rows) requests Q and all of
-// its tiles in one round trip. Waves w and w + 4 share a SIMD; the first four
-// (group A) compute S = K Q^T tile by tile as the tiles land, then the
-// softmax, while group B computes its S; group A's O += V^T P^T then runs
-// beside group B's softmax, so each SIMD's matrix and vector pipes overlap.
-// One softmax per row over the whole split (a single max, no rescaling).
+// its tiles in one round trip (Q through LDS as well, so that every wait is
+// a counted one), and every wave takes each tile through S = K Q^T, an
+// online-softmax step (the tile loop's lazy running max and trial
+// probabilities) and O += V^T P^T as soon as the tile has landed.
 //
 // Blocks are numbered split-major over groups padded to a multiple of 8, so
 // every split of one (request, kv head, row block) -- and, when batch * Hkv
