@@ -477,3 +477,45 @@ def test_anchor_form_splits_starting_in_skipped_tiles_whole_output():
     got = out[rows[:, 0], rows[:, 1]].float().cpu().numpy()
     gl = lse[rows[:, 0], rows[:, 1]].cpu().numpy()
     print("anchor-splits", assert_attn_close(got, ref, "bf16", gl, rlse, what="anchor-splits"))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_sweep(seed):
+    """Seeded random shapes across the plan's branches: batch 1..10, GQA
+    group 1..8 over 1..8 kv heads, head_dim 64 or 128, 16..64-key pages,
+    prefixes 0..2600 keys, random trees of 1..100 nodes (or trunk-and-branch
+    trees in the ANCHOR form), with or without split merges -- every output
+    against the oracle."""
+    rng = np.random.default_rng(1000 + seed)
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    page = int(rng.choice([16, 32, 64]))
+    batch = int(rng.integers(1, 11))
+    anchor = seed % 4 == 3
+    if anchor:
+        trees = []
+        for _ in range(batch):
+            trunk = int(rng.integers(16, 700))
+            na = int(rng.integers(1, 6))
+            anchors = np.sort(rng.choice(np.arange(trunk), size=min(na, trunk), replace=False))
+            trees.append(W.trunk_branch_tree(trunk, anchors.tolist(), int(rng.integers(1, 17))))
+        prefix = [0] * batch
+    else:
+        trees = [W.random_tree(rng, int(rng.integers(1, 101))) for _ in range(batch)]
+        prefix = [int(x) for x in rng.integers(0, 2601, size=batch)]
+    w = W.build_workload("sweep%d" % seed, trees, prefix, hq, hkv, d, "bf16", rng, page_size=page,
+                         permute_pages=bool(rng.integers(0, 2)), spare_pages=2, tokens=False,
+                         mask_kind="anchor" if anchor else "bits")
+    pl = tv.verify_attn_plan(w.batch, w.total_nodes, w.max_nodes, w.max_prefix_len,
+                             w.num_q_heads, w.num_kv_heads, w.head_dim, torch.bfloat16)
+    print("sweep", seed, dict(batch=batch, hq=hq, hkv=hkv, d=d, page=page, anchor=anchor,
+                              nodes=w.total_nodes, max_prefix=w.max_prefix_len), pl, flush=True)
+    d_ = Dev(w)
+    out, lse = d_.attn()
+    torch.cuda.synchronize()
+    ref, rlse = oracle_attn_threaded(w)
+    rows = all_rows(w)
+    got = out[rows[:, 0], rows[:, 1]].float().cpu().numpy()
+    gl = lse[rows[:, 0], rows[:, 1]].cpu().numpy()
+    print("sweep", seed, assert_attn_close(got, ref, "bf16", gl, rlse, what="sweep %d" % seed))
