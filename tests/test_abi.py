@@ -104,6 +104,17 @@ def test_merge_chunk_shapes_reach_every_chunk_size():
     assert all(s not in (2, 4, 8, 16) for s in list(seen.values())[1:]), seen  # unused positions
 
 
+def test_wide_merge_shapes_have_their_split_counts():
+    """The GPU test of the merge with 8 elements a lane (16,384 rows or more,
+    at most 4 splits) uses shapes whose 256-CU plans give 4, 3 and 2 splits."""
+    import test_gpu_2_attn as t2
+    for batch, nodes, keys, splits in t2._WIDE_MERGE_SHAPES:
+        pl = tv.verify_attn_plan(batch, batch * nodes, nodes, keys, 64, 8, 128,
+                                 binding.torch.bfloat16, 256)
+        assert (pl["splits"], pl["rows_per_block"]) == (splits, 256)
+        assert batch * nodes * 64 >= 16384
+
+
 def test_attention_plan_splits_grow_with_the_compute_units():
     s = [tv.verify_attn_plan(1, 60, 60, 2048, 32, 8, 128, binding.torch.bfloat16, c)["splits"]
          for c in (80, 256, 304)]

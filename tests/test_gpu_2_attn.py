@@ -425,18 +425,30 @@ def test_split_merge_chunk_sizes(shape):
 
 
 
-def test_split_merge_256_row_blocks_whole_output():
+# (requests, nodes per tree, keys, splits on 256 CUs): at least 16,384 rows
+# (64 q heads) and at most 4 splits take the merge with 8 elements a lane;
+# 3 splits leave one of its 4 loaded positions unused.
+_WIDE_MERGE_SHAPES = [(4, 64, 3000, 4), (5, 60, 3000, 3), (8, 60, 3000, 2)]
+
+
+@pytest.mark.parametrize("shape", _WIDE_MERGE_SHAPES)
+def test_split_merge_256_row_blocks_whole_output(shape):
     """Key splits of the 256-row tile loop merged over a poisoned workspace
-    (0xFF bytes): 4 requests of a 64-node tree over 3000 keys, 64 q / 8 kv
-    heads (4 splits, 16,384 rows), every output against the oracle."""
-    rng = np.random.default_rng(77)
-    trees = [W.random_tree(rng, 64) for _ in range(4)]
-    w = W.build_workload("merge-256", trees, [3000] * 4, 64, 8, 128, "bf16", rng,
+    (0xFF bytes): requests of a random tree over 3000 keys, 64 q / 8 kv
+    heads (16,384 rows or more, 2 to 4 splits), every output against the
+    oracle."""
+    batch, nodes, keys, splits = shape
+    rng = np.random.default_rng(77 + batch)
+    trees = [W.random_tree(rng, nodes) for _ in range(batch)]
+    w = W.build_workload("merge-256", trees, [keys] * batch, 64, 8, 128, "bf16", rng,
                          permute_pages=True, tokens=False)
     pl = tv.verify_attn_plan(w.batch, w.total_nodes, w.max_nodes, w.max_prefix_len,
                              w.num_q_heads, w.num_kv_heads, w.head_dim, torch.bfloat16)
-    print("merge-256", pl, flush=True)
-    assert pl["splits"] > 1 and pl["rows_per_block"] == 256
+    print("merge-256", shape, pl, flush=True)
+    assert pl["rows_per_block"] == 256 and w.total_nodes * 64 >= 16384
+    if pl["num_cus"] == 256:
+        assert pl["splits"] == splits
+    assert pl["splits"] > 1
     d = Dev(w)
     ws = torch.empty(pl["workspace_bytes"], dtype=torch.uint8, device="cuda")
     ws.fill_(255)
