@@ -1480,6 +1480,67 @@ __global__ __launch_bounds__(256) void combine_kernel(const __bf16* __restrict__
   if (lse && sub == 0) lse[row] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
 }
 
+// The same merge for many rows (at least 16,384, so that the blocks still
+// fill the GPU): 8 elements (16 bytes) a lane, half the lanes and loads.
+template <int D, int CH>
+__global__ __launch_bounds__(256) void combine_wide_kernel(const __bf16* __restrict__ part_o,
+                                                           const float* __restrict__ part_ml,
+                                                           int64_t R_tot, int32_t splits,
+                                                           __bf16* __restrict__ out, float* __restrict__ lse) {
+  constexpr int LPR = D / 8;               // lanes per row
+  constexpr int RPB = 256 / LPR;           // rows per block
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int sub = threadIdx.x % LPR;
+  if (row >= R_tot) return;
+  float m = -INFINITY, l = 0.f;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < splits; s0 += CH) {
+    float2 ml[CH];
+    bf16x8 os[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int64_t pr = (int64_t)min(s0 + j, splits - 1) * R_tot + row;
+      ml[j] = *reinterpret_cast<const float2*>(part_ml + pr * 2);
+      os[j] = *reinterpret_cast<const bf16x8*>(part_o + pr * D + 8 * sub);
+    }
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+      if (s0 + j >= splits) ml[j].x = -INFINITY;
+    float mc = m;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) mc = fmaxf(mc, ml[j].x);
+    const float a = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mc);
+    l *= a;
+    acc0 *= a;
+    acc1 *= a;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const bool live = ml[j].x != -INFINITY;
+      const float w = live ? __builtin_amdgcn_exp2f(ml[j].x - mc) : 0.f;
+      const float wl = w * ml[j].y;
+      l += live ? wl : 0.f;
+      f32x4 o0, o1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o0[i] = static_cast<float>(os[j][i]);
+        o1[i] = static_cast<float>(os[j][4 + i]);
+      }
+      acc0 = live ? acc0 + wl * o0 : acc0;
+      acc1 = live ? acc1 + wl * o1 : acc1;
+    }
+    m = mc;
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  bf16x8 h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = static_cast<__bf16>(acc0[i] * inv);
+    h[4 + i] = static_cast<__bf16>(acc1[i] * inv);
+  }
+  *reinterpret_cast<bf16x8*>(out + row * D + 8 * sub) = h;
+  if (lse && sub == 0) lse[row] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+}
+
 // ------------------------------------------------------------- fp32 path --
 // 4 lanes per (node, head) row, each owning d = 4j + sub; 16 rows per block.
 struct ParamsF32 {
@@ -1656,67 +1717,6 @@ AttnPlan plan_attn(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_
   }
   return pl;
 }
-// The same merge for many rows (at least 16,384, so that the blocks still
-// fill the GPU): 8 elements (16 bytes) a lane, half the lanes and loads.
-template <int D, int CH>
-__global__ __launch_bounds__(256) void combine_wide_kernel(const __bf16* __restrict__ part_o,
-                                                           const float* __restrict__ part_ml,
-                                                           int64_t R_tot, int32_t splits,
-                                                           __bf16* __restrict__ out, float* __restrict__ lse) {
-  constexpr int LPR = D / 8;               // lanes per row
-  constexpr int RPB = 256 / LPR;           // rows per block
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int sub = threadIdx.x % LPR;
-  if (row >= R_tot) return;
-  float m = -INFINITY, l = 0.f;
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < splits; s0 += CH) {
-    float2 ml[CH];
-    bf16x8 os[CH];
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int64_t pr = (int64_t)min(s0 + j, splits - 1) * R_tot + row;
-      ml[j] = *reinterpret_cast<const float2*>(part_ml + pr * 2);
-      os[j] = *reinterpret_cast<const bf16x8*>(part_o + pr * D + 8 * sub);
-    }
-#pragma unroll
-    for (int j = 0; j < CH; ++j)
-      if (s0 + j >= splits) ml[j].x = -INFINITY;
-    float mc = m;
-#pragma unroll
-    for (int j = 0; j < CH; ++j) mc = fmaxf(mc, ml[j].x);
-    const float a = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mc);
-    l *= a;
-    acc0 *= a;
-    acc1 *= a;
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const bool live = ml[j].x != -INFINITY;
-      const float w = live ? __builtin_amdgcn_exp2f(ml[j].x - mc) : 0.f;
-      const float wl = w * ml[j].y;
-      l += live ? wl : 0.f;
-      f32x4 o0, o1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        o0[i] = static_cast<float>(os[j][i]);
-        o1[i] = static_cast<float>(os[j][4 + i]);
-      }
-      acc0 = live ? acc0 + wl * o0 : acc0;
-      acc1 = live ? acc1 + wl * o1 : acc1;
-    }
-    m = mc;
-  }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  bf16x8 h;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    h[i] = static_cast<__bf16>(acc0[i] * inv);
-    h[4 + i] = static_cast<__bf16>(acc1[i] * inv);
-  }
-  *reinterpret_cast<bf16x8*>(out + row * D + 8 * sub) = h;
-  if (lse && sub == 0) lse[row] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
-}
-
 // the merge with the smallest chunk that holds every split (16 at most)
 template <int D>
 hipError_t launch_combine(const Params& p, int splits, int64_t rtot, float* lse, hipStream_t stream) {
