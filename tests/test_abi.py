@@ -207,10 +207,15 @@ def test_graft_argument_checks():
     assert ws(60, 151936, 8, 0) > 0
     assert ws(60, 151936, 8, 3) == 0             # bad dtype: nothing to size
     assert ws(9, 5, 1, 1) == 0 and ws(1, 1, 1, 0) == 0   # below one 16-byte group
-    # a workspace below the size is refused before anything is launched (this
-    # shape splits rows the same way on the 16-byte and the one-value path)
+    # a workspace below what the call's path needs is refused before anything
+    # is launched: 16-byte-aligned bf16 rows take the share kernel (4 shares
+    # of k entries of 8 bytes per node here), other rows the one-value shares
+    # (9 shares per node here); the query covers both
     assert u(FAKE, 151936, 8, FAKE, 1, 60, FAKE, None, 0, None) == 3
-    assert u(FAKE, 151936, 8, FAKE, 1, 60, FAKE, FAKE, need - 1, None) == 3
+    assert u(FAKE, 151936, 8, FAKE, 1, 60, FAKE, FAKE, 60 * 4 * 8 * 8 - 1, None) == 3
+    odd = ctypes.c_void_p(FAKE.value + 2)        # bf16-aligned, not 16-byte aligned
+    assert u(FAKE, 151936, 8, odd, 1, 60, FAKE, FAKE, 60 * 9 * 8 * 8 - 1, None) == 3
+    assert need >= max(60 * 4 * 8 * 8, 60 * 9 * 8 * 8)
 
 
 def test_sampled_accept_argument_checks():

@@ -156,6 +156,63 @@ def test_update_row_shares(n, v, k, dtype, offset):
     np.testing.assert_array_equal(a.cpu().numpy(), oracle.graft_update(adj, exact, toks))
 
 
+def _threshold_rows(rng, v, k):
+    """bf16 rows for the whole-row workgroup's thresholds: each row reaches
+    one branch of its bound T (plain bits, flipped bits for negative tops,
+    the exact wave lists when T bounds nothing)."""
+    rows = []
+    rows.append(rng.normal(-12, 3, size=v))                        # log-probabilities: all < 0
+    r = np.full(v, -np.inf); r[rng.choice(v, k, replace=False)] = rng.normal(0, 1, k)
+    rows.append(r)                                                 # exactly k finite values
+    r = np.full(v, -np.inf); r[rng.choice(v, max(k - 1, 0), replace=False)] = 1.5
+    rows.append(r)                                                 # fewer than k finite: -inf ties
+    r = rng.normal(-5, 1, size=v); at = rng.choice(v, 10, replace=False)
+    r[at[:5]] = 0.0; r[at[5:]] = -0.0
+    rows.append(r)                                                 # +0 and -0 on top
+    r = rng.normal(0, 1, size=v); r[rng.choice(v, 1000, replace=False)] = 7.0
+    rows.append(r)                                                 # a plateau of 1000 equal tops
+    r = rng.normal(0, 3, size=v); r[rng.random(v) < 0.05] = np.nan
+    rows.append(r)                                                 # positive NaNs
+    r = rng.normal(0, 3, size=v); r[rng.random(v) < 0.05] = -np.nan
+    rows.append(r)                                                 # negative NaNs
+    r = rng.normal(0, 1, size=v); r[rng.random(v) < 0.5] = np.inf
+    rows.append(r)                                                 # +inf everywhere
+    r = rng.normal(0, 1, size=v); r[rng.choice(v, 3, replace=False)] = np.inf
+    rows.append(r)                                                 # a few +inf on top
+    r = np.full(v, -np.inf); r[rng.choice(v, 5, replace=False)] = np.nan
+    rows.append(r)                                                 # -inf and NaN only
+    r = rng.normal(0, 3, size=v); top = np.argsort(-r)[:k + 3]; r[top] = r[top[0]]
+    rows.append(r)                                                 # k + 3 ties at the maximum
+    r = -np.abs(rng.normal(0, 1e-3, size=v)); r[rng.choice(v, 20, replace=False)] = -0.0
+    rows.append(r)                                                 # negative tops near -0
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("v,k", [(151936, 8), (151936, 16), (151936, 1), (5000, 8)])
+def test_update_whole_row_thresholds(v, k):
+    """Rows of one workgroup each (bf16, 16-byte aligned, vocabulary a multiple
+    of 8): every table row against the oracle, for rows built to reach each
+    way the row's bound T is found or refused."""
+    rng = np.random.default_rng(v + 31 * k)
+    logits = _threshold_rows(rng, v, k)
+    n = logits.shape[0]
+    adj = _table(rng, v, k)
+    toks = rng.permutation(v)[:n].astype(np.int32)
+    lg = torch.from_numpy(logits).to(torch.bfloat16)
+    bits = lg.view(torch.int16)                            # NaN bits set from numpy's sign
+    nan = np.isnan(logits)
+    neg_nan = torch.from_numpy(nan & np.signbit(logits))
+    pos_nan = torch.from_numpy(nan & ~np.signbit(logits))
+    bits[neg_nan] = np.int16(-64)                          # 0xffc0
+    bits[pos_nan] = np.int16(0x7fc0)
+    assert int(neg_nan.sum()) > 0 and int(pos_nan.sum()) > 0
+    a = torch.from_numpy(adj.copy()).cuda()
+    tv.graft_update(a, lg.cuda(), torch.from_numpy(toks).cuda())
+    torch.cuda.synchronize()
+    exact = lg.float().numpy()
+    np.testing.assert_array_equal(a.cpu().numpy(), oracle.graft_update(adj, exact, toks))
+
+
 def test_update_many_nodes_one_workgroup_per_row():
     # thousands of verified nodes: one workgroup per row, many repeated tokens
     rng = np.random.default_rng(45)

@@ -12,11 +12,14 @@ namespace tv {
 // multiple of W -- else a single value.
 template <typename T, bool VEC>
 struct VocabUnit;
+// `fetch` returns the unit's raw bits and `unpack` converts them, so that a
+// kernel can keep many units in flight in few registers.
 template <>
 struct VocabUnit<__bf16, true> {
   static constexpr int W = 8;
-  __device__ static void load(const __bf16* p, float (&y)[W]) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
+  using Raw = uint4;
+  __device__ static Raw fetch(const __bf16* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ static void unpack(const Raw& u, float (&y)[W]) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -24,18 +27,24 @@ struct VocabUnit<__bf16, true> {
       y[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   }
+  __device__ static void load(const __bf16* p, float (&y)[W]) { unpack(fetch(p), y); }
 };
 template <>
 struct VocabUnit<float, true> {
   static constexpr int W = 4;
-  __device__ static void load(const float* p, float (&y)[W]) {
-    const float4 u = *reinterpret_cast<const float4*>(p);
+  using Raw = float4;
+  __device__ static Raw fetch(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ static void unpack(const Raw& u, float (&y)[W]) {
     y[0] = u.x; y[1] = u.y; y[2] = u.z; y[3] = u.w;
   }
+  __device__ static void load(const float* p, float (&y)[W]) { unpack(fetch(p), y); }
 };
 template <typename T>
 struct VocabUnit<T, false> {
   static constexpr int W = 1;
+  using Raw = T;
+  __device__ static Raw fetch(const T* p) { return *p; }
+  __device__ static void unpack(const Raw& u, float (&y)[W]) { y[0] = static_cast<float>(u); }
   __device__ static void load(const T* p, float (&y)[W]) { y[0] = static_cast<float>(*p); }
 };
 template <typename T>
