@@ -213,6 +213,49 @@ def test_update_whole_row_thresholds(v, k):
     np.testing.assert_array_equal(a.cpu().numpy(), oracle.graft_update(adj, exact, toks))
 
 
+def _mixed_row(rng, v):
+    kind = rng.integers(0, 6)
+    if kind == 0:
+        return rng.normal(0, 3, size=v)
+    if kind == 1:
+        return rng.normal(-20, 2, size=v)                                # all negative
+    if kind == 2:
+        return np.round(rng.normal(0, 2, size=v))                        # many ties
+    if kind == 3:
+        r = np.full(v, -np.inf)
+        m = int(rng.integers(0, 40))
+        r[rng.choice(v, m, replace=False)] = rng.normal(0, 1, m)         # few finite values
+        return r
+    r = rng.normal(0, 1, size=v)
+    r[rng.random(v) < 0.02] = rng.choice([np.nan, np.inf, -np.inf, 0.0, -0.0])
+    if kind == 5:
+        r[rng.integers(0, v)] = np.inf
+    return r
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_update_share_boundaries_sweep(seed):
+    """Seeded sweep of the bf16 share path: vocabularies around multiples of
+    one share (40,960 entries), 1 to 8 shares, k in 1..16 within the list
+    kernel's 64 entries, rows of mixed kinds (normal, all negative, ties,
+    few finite values, scattered NaN / +-inf / +-0), repeated tokens; every
+    table row against the oracle."""
+    rng = np.random.default_rng(900 + seed)
+    share = 40960
+    shares = int(rng.integers(1, 9))
+    v = 8 * int(rng.integers(max(1, (shares - 1) * share // 8 + 1), shares * share // 8 + 1))
+    k = int(rng.integers(1, min(16, 64 // shares) + 1))
+    n = int(rng.integers(1, 40))
+    logits = np.stack([_mixed_row(rng, v) for _ in range(n)]).astype(np.float32)
+    adj = _table(rng, v, k)
+    toks = rng.integers(0, v, size=n).astype(np.int32)
+    if n > 3:
+        toks[n - 1] = toks[1]
+    print("sweep", seed, dict(v=v, k=k, n=n, shares=shares), flush=True)
+    got, exact = _update(adj, logits, toks, torch.bfloat16)
+    np.testing.assert_array_equal(got, oracle.graft_update(adj, exact, toks))
+
+
 def test_update_many_nodes_one_workgroup_per_row():
     # thousands of verified nodes: one workgroup per row, many repeated tokens
     rng = np.random.default_rng(45)
