@@ -252,11 +252,12 @@ __global__ __launch_bounds__(kUpdateThreads) void graft_topk_kernel(
 }
 
 // graft_share_kernel + graft_lists_kernel (bf16 rows, 16-byte aligned, the
-// vocabulary a multiple of 8): each node's row is cut into at most
-// kShareMax shares of at most kShareUnits 16-byte units, one 256-thread
-// workgroup each, every unit of the share requested at once and before the
-// ownership test's tokens are back. A row needs several compute units at a
-// time: one compute unit alone streams a 151,936-entry row in about 10 us.
+// vocabulary a multiple of 8): each node's row is cut into the fewest
+// shares of at most kShareUnits 16-byte units a thread (at most
+// kListLanes / k shares), one 256-thread workgroup each, every unit of the
+// share requested at once and before the ownership test's tokens are back.
+// A row needs several compute units at a time: one compute unit alone
+// streams a 151,936-entry row in about 10 us.
 //
 // Selection in a share: each unit gets a 16-bit key that orders like its
 // largest value -- the raw bf16 bits compared as signed integers where the
