@@ -1701,6 +1701,9 @@ AttnPlan plan_attn(int32_t batch, int32_t total_nodes, int32_t max_nodes, int32_
   const long max_tps = (long)(kMaxSplitPages - 8) * 16 / kTile;
   splits = std::max(splits, (tiles + max_tps - 1) / max_tps);
   const long tps = (tiles + splits - 1) / splits;
+  // whole 64-key tiles per split: the kernels mask only keys past the
+  // request's end, so a split ending inside a tile would also count the next
+  // split's keys in that tile
   pl.keys_per_split = (int)(tps * kTile);
   pl.splits = (int)((tiles + tps - 1) / tps);
   // splits of a few tiles take the one-shot kernel (128-row blocks)
