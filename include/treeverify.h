@@ -454,8 +454,10 @@ tv_status_t tv_tree_accept_sampled(const int32_t* parent, const int32_t* draft_t
                                    int32_t* accept_len, int32_t* path, int32_t* bonus_tok,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Static description of a status code. */
-const char* tv_status_string(tv_status_t status);
+/* Static description of a status code: status is a tv_status_t value (taken
+ * as a plain integer, so that any other value is defined input and gives
+ * "unknown status"). */
+const char* tv_status_string(int32_t status);
 
 #ifdef __cplusplus
 }

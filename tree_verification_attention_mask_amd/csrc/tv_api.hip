@@ -43,7 +43,7 @@ inline int32_t plan_cus() {
 }
 }  // namespace
 
-extern "C" const char* tv_status_string(tv_status_t s) {
+extern "C" const char* tv_status_string(int32_t s) {
   switch (s) {
     case TV_OK: return "ok";
     case TV_ERR_INVALID_ARGUMENT: return "invalid argument";
