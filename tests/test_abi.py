@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import tree_verification_attention_mask_amd as tv
@@ -113,6 +114,26 @@ def test_wide_merge_shapes_have_their_split_counts():
                                  binding.torch.bfloat16, 256)
         assert (pl["splits"], pl["rows_per_block"]) == (splits, 256)
         assert batch * nodes * 64 >= 16384
+
+
+def test_attention_plan_splits_are_whole_tiles():
+    """Every plan's key splits are whole 64-key tiles and cover the longest
+    request's keys once: the kernels mask only keys past a request's end, so
+    a split ending inside a tile would also count the next split's keys."""
+    rng = np.random.default_rng(8)
+    for _ in range(400):
+        batch = int(rng.integers(1, 65))
+        max_nodes = int(rng.integers(1, 300))
+        total = batch * int(rng.integers(1, max_nodes + 1))
+        P = int(rng.integers(0, 70000))
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        hq = hkv * int(rng.choice([1, 2, 4, 8]))
+        d = int(rng.choice([64, 128]))
+        cus = int(rng.choice([80, 256, 304]))
+        pl = tv.verify_attn_plan(batch, total, max_nodes, P, hq, hkv, d, binding.torch.bfloat16, cus)
+        kps, splits = pl["keys_per_split"], pl["splits"]
+        assert kps % 64 == 0 and kps > 0, pl
+        assert (splits - 1) * kps < P + max_nodes <= splits * kps, (P, max_nodes, pl)
 
 
 def test_attention_plan_splits_grow_with_the_compute_units():
