@@ -278,7 +278,7 @@ constexpr int kShareThreads = 256;
 constexpr int kShareWaves = kShareThreads / 64;
 constexpr int kShareUnits = 20;                 // units a thread
 constexpr int kShareCap = 256;                  // listed elements (>= 16 per wave)
-constexpr int kListLanes = 64;                  // shares * k
+constexpr int kListLanes = 64;                  // shares * k at most: one entry a lane of graft_lists_kernel
 constexpr int kKeyLo = -32768;                  // below every key
 
 using short2v = short __attribute__((ext_vector_type(2)));
