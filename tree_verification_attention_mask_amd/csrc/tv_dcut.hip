@@ -10,12 +10,18 @@
 // One workgroup of 1024 threads (the ranked set is at most 32768 positions,
 // held in LDS as fp32 bit patterns -- non-negative floats order like their
 // bits):
-//   1. scores: each thread walks its requests' blocks left to right in fp32;
+//   1. scores: the confidences come into LDS in one round trip (every load in
+//      flight), then each thread walks its requests' blocks left to right in
+//      fp32, the products replacing the confidences;
 //   2. threshold: the R-th largest score (R = budget - batch ranked slots) by
-//      a radix select, 8 bits per pass from the top, with an LDS histogram;
+//      a radix select, 8 bits per pass from the top, with an LDS histogram
+//      (two alternating, two barriers a pass);
 //   3. per request: positions above the threshold, plus positions equal to it
 //      handed out in request order (a block scan) -- the tie rule;
-//   4. cu_nodes by a second block scan, then the packed chains and tokens.
+//   4. cu_nodes by a second block scan, then the packed chains and tokens:
+//      with one request per thread (at most 1024), every packed slot finds
+//      its request by a binary search over the requests' first slots and
+//      loads its token, all at once; beyond, each thread packs its requests.
 // Threads own contiguous runs of requests, so scans keep request order.
 #include "tv_launch.h"
 
@@ -59,25 +65,44 @@ __global__ __launch_bounds__(kDcutThreads) void dcut_select_kernel(
     int32_t D, int32_t budget, int32_t* __restrict__ n_keep, int32_t* __restrict__ cu_nodes,
     int32_t* __restrict__ parent, int32_t* __restrict__ packed_tokens) {
   extern __shared__ uint32_t s_key[];  // [batch * D] score bits, request-major
-  __shared__ int s_hist[256];
+  __shared__ int s_hist[2][256];  // two passes' histograms alternate
   __shared__ int s_wave[kDcutWaves + 1];
-  __shared__ uint32_t s_digit;
-  __shared__ int s_rem;
+  __shared__ uint32_t s_digit[2];
+  __shared__ int s_rem[2];
   const int tid = threadIdx.x;
   const int M = batch * D;
   const int R = budget - batch;  // slots ranked among the draft positions
   const int chunk = (batch + kDcutThreads - 1) / kDcutThreads;
   const int b_lo = min(batch, tid * chunk), b_hi = min(batch, b_lo + chunk);
-  if (tid == 0) { s_digit = 0; s_rem = 0; }
+  if (tid == 0) { s_digit[0] = s_digit[1] = 0; s_rem[0] = s_rem[1] = 0; }
+  if (tid < 256) s_hist[0][tid] = 0;  // the first pass's histogram
 
-  // 1. scores, left to right along each block (confidences are probabilities)
+  // 1. scores, left to right along each block (confidences are probabilities):
+  // the confidences come into the score array in one round trip (every load
+  // in flight), then each block's products replace them in place
+  for (int i = tid; i < M; i += kDcutThreads) s_key[i] = __float_as_uint(conf[i]);
+  __syncthreads();
+  auto clamp01 = [](uint32_t bits) {
+    const float c = __uint_as_float(bits);
+    return (c > 0.f) ? fminf(c, 1.f) : 0.f;  // NaN -> 0
+  };
   for (int b = b_lo; b < b_hi; ++b) {
     float s = 1.f;
-    for (int k = 0; k < D; ++k) {
-      float c = conf[(size_t)b * D + k];
-      c = (c > 0.f) ? fminf(c, 1.f) : 0.f;
-      s = __fmul_rn(s, c);
-      s_key[b * D + k] = __float_as_uint(s);
+    uint32_t* row = s_key + b * D;
+    int k = 0;
+    for (; k + 4 <= D; k += 4) {
+      uint32_t c[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j] = row[k + j];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s = __fmul_rn(s, clamp01(c[j]));
+        row[k + j] = __float_as_uint(s);
+      }
+    }
+    for (; k < D; ++k) {
+      s = __fmul_rn(s, clamp01(row[k]));
+      row[k] = __float_as_uint(s);
     }
   }
   __syncthreads();
@@ -89,14 +114,17 @@ __global__ __launch_bounds__(kDcutThreads) void dcut_select_kernel(
   if (some) {
     uint32_t prefix = 0, hmask = 0;
     int remaining = R;  // keys still to take among those matching prefix
+    // two barriers a pass: the next pass's histogram is cleared while this
+    // one fills (it was last read before this pass began), and the picked
+    // digit alternates between two slots
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-      if (tid < 256) s_hist[tid] = 0;
-      __syncthreads();
+      const int buf = pass & 1;
       for (int i = tid; i < M; i += kDcutThreads) {
         const uint32_t key = s_key[i];
-        if ((key & hmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1);
+        if ((key & hmask) == prefix) atomicAdd(&s_hist[buf][(key >> shift) & 255u], 1);
       }
+      if (tid < 256) s_hist[buf ^ 1][tid] = 0;
       __syncthreads();
       if (tid < 64) {
         // lane l owns digits 255-4l .. 252-4l, largest first; the lane whose
@@ -104,7 +132,7 @@ __global__ __launch_bounds__(kDcutThreads) void dcut_select_kernel(
         int c[4], loc = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          c[j] = s_hist[255 - 4 * tid - j];
+          c[j] = s_hist[buf][255 - 4 * tid - j];
           loc += c[j];
         }
         int x = loc;
@@ -117,8 +145,8 @@ __global__ __launch_bounds__(kDcutThreads) void dcut_select_kernel(
         if (acc < remaining && remaining <= x) {
           for (int j = 0; j < 4; ++j) {
             if (acc + c[j] >= remaining) {
-              s_digit = (uint32_t)(255 - 4 * tid - j);
-              s_rem = remaining - acc;
+              s_digit[buf] = (uint32_t)(255 - 4 * tid - j);
+              s_rem[buf] = remaining - acc;
               break;
             }
             acc += c[j];
@@ -126,10 +154,9 @@ __global__ __launch_bounds__(kDcutThreads) void dcut_select_kernel(
         }
       }
       __syncthreads();
-      prefix |= s_digit << shift;
+      prefix |= s_digit[buf] << shift;
       hmask |= 0xffu << shift;
-      remaining = s_rem;
-      __syncthreads();
+      remaining = s_rem[buf];
     }
     tau = prefix;
     rem = remaining;
@@ -142,10 +169,21 @@ __global__ __launch_bounds__(kDcutThreads) void dcut_select_kernel(
     eq = 0;
     if (R >= M) { gt = D; return; }
     if (!some) return;
-    for (int k = 0; k < D; ++k) {
-      const uint32_t key = s_key[b * D + k];
-      gt += key > tau ? 1 : 0;
-      eq += key == tau ? 1 : 0;
+    const uint32_t* row = s_key + b * D;
+    int k = 0;
+    for (; k + 4 <= D; k += 4) {
+      uint32_t v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = row[k + j];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        gt += v[j] > tau ? 1 : 0;
+        eq += v[j] == tau ? 1 : 0;
+      }
+    }
+    for (; k < D; ++k) {
+      gt += row[k] > tau ? 1 : 0;
+      eq += row[k] == tau ? 1 : 0;
     }
   };
 
@@ -173,16 +211,43 @@ __global__ __launch_bounds__(kDcutThreads) void dcut_select_kernel(
 
   // 4. offsets, then the packed chains and tokens
   const int n_before = block_exclusive_sum(local_n, s_wave, total);
-  int eq_run = eq_before, off = n_before;
-  for (int b = b_lo; b < b_hi; ++b) {
-    const int n = kept(b, eq_run);
-    n_keep[b] = n;
-    cu_nodes[b] = off;
-    for (int k = 0; k < n && off + k < budget; ++k) {  // (bounded whatever the counts)
-      parent[off + k] = k - 1;
-      packed_tokens[off + k] = tokens[(size_t)b * (D + 1) + k];
+  if (chunk != 1) {
+    // several requests per thread: each packs its own in order
+    int eq_run = eq_before, off = n_before;
+    for (int b = b_lo; b < b_hi; ++b) {
+      const int n = kept(b, eq_run);
+      n_keep[b] = n;
+      cu_nodes[b] = off;
+      for (int k = 0; k < n && off + k < budget; ++k) {  // (bounded whatever the counts)
+        parent[off + k] = k - 1;
+        packed_tokens[off + k] = tokens[(size_t)b * (D + 1) + k];
+      }
+      off += n;
     }
-    off += n;
+    if (tid == 0) cu_nodes[batch] = total;
+    return;
+  }
+  // one request per thread: the requests' first slots replace the scores in
+  // LDS, and every packed slot finds its request by a binary search and loads
+  // its token (every slot's load in flight at once)
+  if (b_lo < b_hi) {
+    int eq_run = eq_before;
+    n_keep[b_lo] = kept(b_lo, eq_run);
+    cu_nodes[b_lo] = n_before;
+  }
+  __syncthreads();  // every count has read the scores
+  if (b_lo < b_hi) s_key[b_lo] = (uint32_t)n_before;
+  __syncthreads();
+  const int slots = min(total, budget);
+  for (int o = tid; o < slots; o += kDcutThreads) {
+    int lo = 0, hi = batch - 1;  // the last request whose first slot is <= o
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int)s_key[mid] <= o) lo = mid; else hi = mid - 1;
+    }
+    const int k = o - (int)s_key[lo];
+    parent[o] = k - 1;
+    packed_tokens[o] = tokens[(size_t)lo * (D + 1) + k];
   }
   if (tid == 0) cu_nodes[batch] = total;
 }
