@@ -110,8 +110,22 @@ __global__ __launch_bounds__(256) void branch_kernel(const float* __restrict__ a
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= nb) return;
   const int lo = clampi(cu[b], 0, num_nodes), hi = clampi(cu[b + 1], lo, num_nodes);
+  // the same left-to-right products; eight alphas requested at a time (a
+  // loop of one load per step waited for each)
   float run = 1.f, sum = 0.f;
-  for (int i = lo; i < hi; ++i) {
+  int i = lo;
+  for (; i + 8 <= hi; i += 8) {
+    float a8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a8[j] = alpha[i + j];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      run *= a8[j];
+      prefix[i + j] = run;
+      sum += run;
+    }
+  }
+  for (; i < hi; ++i) {
     run *= alpha[i];
     prefix[i] = run;
     sum += run;
